@@ -1,0 +1,162 @@
+"""Integer model of the DCP shared virtual KV layout (oracle; test infrastructure only).
+
+Follows the SGLang page "Decode Context Parallelism", section "Virtual KV
+layout": each rank has physical capacity C tokens in pages of P tokens; the
+group exposes one shared virtual allocator with capacity C*c and page size
+P*c; a virtual slot v belongs to rank owner(v) = v mod c and sits there at
+physical slot physical(v) = floor(v / c).  Every rank sees the same
+request-to-token map; on a write each rank keeps the positions it owns and
+compacts them into its own pool.  The vLLM page "Context Parallel Deployment"
+(section "Decode Context Parallel") gives the user-visible block size as the
+physical block times the DCP size (16 tokens at DCP 4 cover 64 tokens).
+
+Readings where the pages are silent (the allocator's policy and the call
+contract are not on the pages; these fix the one exact answer the bit-exact
+checks compare against):
+
+* A virtual page id is a page index shared by all owner pools: virtual page
+  g covers virtual slots [g*P*c, (g+1)*P*c) and, on every rank, physical
+  slots [g*P, (g+1)*P).
+* Pages are popped from the top of a caller-supplied free stack, in
+  (request, logical page) order; a call that cannot be satisfied takes no
+  page at all (all-or-nothing).
+* New rows of request b occupy the last n_b positions before seq_len[b].
+* Interleave size is one token: owner(p) depends on p mod c only.
+
+Status codes mirror the library's documented device status values; they are
+restated here rather than imported.
+"""
+from __future__ import annotations
+
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+OK = 0
+OUT_OF_PAGES = 1
+BAD_LENGTH = 2
+TABLE_OVERFLOW = 3
+BAD_PAGE = 4
+
+
+def owner(v: int, c: int) -> int:
+    return v % c
+
+
+def physical(v: int, c: int) -> int:
+    return v // c
+
+
+def virtual_page_size(P: int, c: int) -> int:
+    return P * c
+
+
+def virtual_capacity(C: int, c: int) -> int:
+    return C * c
+
+
+def pages_for(length: int, P: int, c: int) -> int:
+    """Virtual pages that hold ``length`` tokens (ceil(length / (P*c)))."""
+    vp = P * c
+    return (length + vp - 1) // vp
+
+
+def virtual_slot(bt_row: Sequence[int], p: int, P: int, c: int) -> int:
+    """Virtual slot of logical position p of a request whose pages are bt_row."""
+    vp = P * c
+    return int(bt_row[p // vp]) * vp + p % vp
+
+
+def slot_of(bt_row: Sequence[int], p: int, P: int, c: int) -> Tuple[int, int]:
+    """(owner rank, physical slot in that rank's pool) of logical position p."""
+    v = virtual_slot(bt_row, p, P, c)
+    return owner(v, c), physical(v, c)
+
+
+def alloc_virtual(free_stack: np.ndarray, free_top: int, old_len: Sequence[int],
+                  new_len: Sequence[int], block_table: np.ndarray, P: int, c: int):
+    """Grow every request from old_len to new_len tokens.
+
+    Returns ``(status, free_top, block_table)``; on any error nothing changes.
+    """
+    bt = np.array(block_table, copy=True)
+    stride = bt.shape[1]
+    B = len(old_len)
+    for b in range(B):
+        if old_len[b] < 0 or new_len[b] < old_len[b]:
+            return BAD_LENGTH, free_top, np.array(block_table, copy=True)
+    for b in range(B):
+        if pages_for(int(new_len[b]), P, c) > stride:
+            return TABLE_OVERFLOW, free_top, np.array(block_table, copy=True)
+    need = [pages_for(int(new_len[b]), P, c) - pages_for(int(old_len[b]), P, c) for b in range(B)]
+    if sum(need) > free_top:
+        return OUT_OF_PAGES, free_top, np.array(block_table, copy=True)
+    top = free_top
+    for b in range(B):
+        first = pages_for(int(old_len[b]), P, c)
+        for i in range(need[b]):
+            top -= 1
+            bt[b, first + i] = free_stack[top]
+    return OK, top, bt
+
+
+def write_slots(block_table: np.ndarray, seq_len: Sequence[int], cu_new: Sequence[int],
+                P: int, c: int, num_pages: int):
+    """Destination of every new row: (status, owner[N], phys[N]); -1 where skipped."""
+    B = len(seq_len)
+    N = int(cu_new[B])
+    own = np.full(N, -1, dtype=np.int64)
+    phys = np.full(N, -1, dtype=np.int64)
+    status = OK
+    stride = block_table.shape[1]
+    for b in range(B):
+        n_b = int(cu_new[b + 1]) - int(cu_new[b])
+        first = int(seq_len[b]) - n_b
+        for k in range(max(n_b, 0)):
+            row = int(cu_new[b]) + k
+            p = first + k
+            if first < 0:
+                status = max(status, BAD_LENGTH)
+                continue
+            if p // (P * c) >= stride:
+                status = max(status, TABLE_OVERFLOW)
+                continue
+            page = int(block_table[b, p // (P * c)])
+            if page < 0 or page >= num_pages:
+                status = max(status, BAD_PAGE)
+                continue
+            r, s = slot_of(block_table[b], p, P, c)
+            own[row], phys[row] = r, s
+    return status, own, phys
+
+
+def pool_image(pools: np.ndarray, block_table: np.ndarray, seq_len, cu_new, rows: np.ndarray,
+               P: int, c: int, scales: np.ndarray = None, pool_scales: np.ndarray = None):
+    """Expected pool bytes after scattering ``rows`` into a copy of ``pools``.
+
+    ``pools`` is [c][num_pages*P][row elements] in the stored dtype.
+    """
+    out = np.array(pools, copy=True)
+    outs = None if pool_scales is None else np.array(pool_scales, copy=True)
+    num_pages = out.shape[1] // P
+    status, own, phys = write_slots(block_table, seq_len, cu_new, P, c, num_pages)
+    for n in range(len(own)):
+        if own[n] >= 0:
+            out[own[n], phys[n]] = rows[n]
+            if outs is not None:
+                outs[own[n], phys[n]] = scales[n]
+    return status, own, phys, out, outs
+
+
+def owned_positions(length: int, c: int, r: int) -> np.ndarray:
+    """Logical positions of a request of ``length`` tokens that rank r owns, ascending."""
+    return np.array([p for p in range(length) if owner(p, c) == r], dtype=np.int64)
+
+
+def owned_count(length: int, c: int, r: int) -> int:
+    return sum(1 for p in range(length) if p % c == r)
+
+
+def rank_local_slots(block_table_row: Sequence[int], length: int, P: int, c: int, r: int) -> List[int]:
+    """Physical slots, in rank r's pool, of the positions r owns, in position order."""
+    return [slot_of(block_table_row, int(p), P, c)[1] for p in owned_positions(length, c, r)]

@@ -1,0 +1,156 @@
+"""Pins for the oracle's integer layout model (CPU only).
+
+Literal vectors come from the pages (tests/golden/stripes.json, each with its
+citation); the rest is brute-force enumeration of small groups against the
+closed forms owner(v) = v mod c, physical(v) = floor(v/c), plus the balance
+property that one widened virtual page maps to one physical page on every rank.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import layout
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def test_dcp4_diagram_vectors():
+    g = _gold("stripes.json")["dcp4_diagram"]
+    for r, want in enumerate(g["owned"]):
+        assert list(layout.owned_positions(g["tokens"], g["c"], r)) == want
+
+
+def test_dcp4_4096_prefix_and_share():
+    g = _gold("stripes.json")["dcp4_4096_prefix"]
+    for r, want in enumerate(g["owned_prefix"]):
+        got = layout.owned_positions(g["tokens"], g["c"], r)
+        assert list(got[:3]) == want
+        assert len(got) == g["owned_count"]
+
+
+def test_effective_block_size():
+    g = _gold("stripes.json")["effective_block"]
+    assert layout.virtual_page_size(g["P"], g["c"]) == g["virtual_page"]
+
+
+def test_allocator_hand_worked_example():
+    # P=2, c=2 -> virtual page of 4 tokens.  Request 0 grows 0 -> 5 tokens (2 pages),
+    # request 1 grows 3 -> 9 tokens (from 1 page to 3).  Pops come off the top of the
+    # stack in (request, page) order: 8, 6 for request 0, then 4, 2 for request 1.
+    stack = np.array([5, 3, 9, 1, 7, 0, 2, 4, 6, 8], dtype=np.int32)
+    bt = np.full((2, 4), -1, dtype=np.int32)
+    bt[1, 0] = 11
+    st, top, out = layout.alloc_virtual(stack, 10, [0, 3], [5, 9], bt, P=2, c=2)
+    assert st == layout.OK and top == 6
+    assert out.tolist() == [[8, 6, -1, -1], [11, 4, 2, -1]]
+
+
+@pytest.mark.parametrize("old,new,top,stride,want", [
+    ([0, 0], [9, 9], 4, 4, layout.OUT_OF_PAGES),       # needs 3 + 3 > 4
+    ([4, 0], [3, 1], 10, 4, layout.BAD_LENGTH),         # shrinking
+    ([0, 0], [17, 1], 10, 4, layout.TABLE_OVERFLOW),    # 5 pages > stride 4
+])
+def test_allocator_errors_change_nothing(old, new, top, stride, want):
+    stack = np.arange(10, dtype=np.int32)
+    bt = np.full((2, stride), -7, dtype=np.int32)
+    st, t2, out = layout.alloc_virtual(stack, top, old, new, bt, P=2, c=2)
+    assert st == want and t2 == top and np.array_equal(out, bt)
+
+
+def _grow(rng, c, P, lens_final, steps):
+    """Grow a batch step by step through the allocator; returns block table and stack."""
+    B = len(lens_final)
+    vp = P * c
+    num_pages = sum((L + vp - 1) // vp for L in lens_final) + 2
+    stack = rng.permutation(num_pages).astype(np.int32)
+    top = num_pages
+    stride = max((L + vp - 1) // vp for L in lens_final) + 1
+    bt = np.full((B, stride), -1, dtype=np.int32)
+    cur = [0] * B
+    for s in range(1, steps + 1):
+        new = [min(L, (L * s) // steps) for L in lens_final]
+        st, top, bt = layout.alloc_virtual(stack, top, cur, new, bt, P, c)
+        assert st == layout.OK
+        cur = new
+    return bt, num_pages
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_slot_map_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    c = int(rng.integers(1, 9))
+    P = int(rng.integers(1, 5))
+    B = int(rng.integers(1, 4))
+    lens = [int(x) for x in rng.integers(0, 200, size=B)]
+    bt, num_pages = _grow(rng, c, P, lens, steps=int(rng.integers(1, 6)))
+    C = num_pages * P
+    seen = set()
+    for b, L in enumerate(lens):
+        for p in range(L):
+            r, s = layout.slot_of(bt[b], p, P, c)
+            assert r == p % c                       # interleave of one token
+            assert 0 <= s < C
+            assert (r, s) not in seen               # no two tokens share a slot
+            seen.add((r, s))
+        # the rank-local walk over owned positions uses the shared table directly:
+        # the j-th owned position of rank r sits at bt[j // P] * P + j % P
+        for r in range(c):
+            want = [int(bt[b, j // P]) * P + j % P for j in range(layout.owned_count(L, c, r))]
+            assert layout.rank_local_slots(bt[b], L, P, c, r) == want
+
+
+@pytest.mark.parametrize("c,P", [(1, 4), (2, 3), (4, 16), (8, 2), (5, 7)])
+def test_balance_within_one_token(c, P):
+    for L in range(0, 300):
+        counts = [layout.owned_count(L, c, r) for r in range(c)]
+        assert max(counts) - min(counts) <= 1
+        assert sum(counts) == L
+    # one widened virtual page is one physical page on every rank: each rank stores its
+    # share in (a prefix of) the request's own virtual pages, in the same page ids, and
+    # page counts differ by at most one (only the partial last page can be missing)
+    rng = np.random.default_rng(c * 10 + P)
+    for L in [1, P * c - 1, P * c, P * c + 1, 5 * P * c + 3]:
+        bt, _ = _grow(rng, c, P, [L], steps=3)
+        vpages = [int(x) for x in bt[0, :layout.pages_for(L, P, c)]]
+        for r in range(c):
+            pg = []
+            for s in layout.rank_local_slots(bt[0], L, P, c, r):
+                if not pg or pg[-1] != s // P:
+                    pg.append(s // P)
+            assert pg == vpages[:len(pg)]
+            assert len(vpages) - len(pg) <= 1
+
+
+def test_write_slots_positions_and_errors():
+    c, P = 2, 2
+    bt = np.array([[3, 1, -1], [0, 9, -1]], dtype=np.int32)
+    # request 0 appends 3 rows ending at length 6 (positions 3,4,5); request 1 appends 1 row at 5
+    st, own, phys = layout.write_slots(bt, [6, 5], [0, 3, 4], P, c, num_pages=4)
+    assert st == layout.BAD_PAGE                         # page 9 >= 4 pages
+    assert own.tolist() == [1, 0, 1, -1]
+    # position 3: v = 3*4 + 3 = 15 -> owner 1, phys 7 ; position 4: v = 1*4 + 0 -> owner 0, phys 2
+    assert phys.tolist() == [7, 2, 2, -1]
+    st, _, _ = layout.write_slots(bt, [2, 0], [0, 3, 3], P, c, num_pages=4)
+    assert st == layout.BAD_LENGTH
+
+
+def test_pool_image_sentinel_untouched():
+    c, P = 2, 2
+    bt = np.array([[1, 0]], dtype=np.int32)
+    pools = np.full((c, 2 * P, 3), 0xEE, dtype=np.uint8)
+    rows = np.arange(15, dtype=np.uint8).reshape(5, 3)
+    st, own, phys, out, _ = layout.pool_image(pools, bt, [5], [0, 5], rows, P, c)
+    assert st == layout.OK
+    written = {(int(o), int(s)) for o, s in zip(own, phys)}
+    for r in range(c):
+        for s in range(2 * P):
+            if (r, s) not in written:
+                assert (out[r, s] == 0xEE).all()      # a partial last page leaks nothing
+    assert len(written) == 5

@@ -1,0 +1,52 @@
+"""Algorithmic bytes and FLOPs of one DCP MLA-decode layer-step.
+
+The counting rules follow the vLLM GLM-5.3 blog post (section "Why the
+numbers add up"): each (KV row, query head) pair costs 2*576 FLOPs for QK and
+2*512 for PV, 2176 in all, softmax not counted; bf16 query and output add
+2*576 + 2*512 = 2176 bytes per head; each KV row is read once for all heads.
+Those footnote figures are reproduced in the tests to pin these functions.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .configs import D_QK, D_V, Workload
+
+
+def flops_per_score(d_qk: int = D_QK, d_v: int = D_V) -> int:
+    return 2 * d_qk + 2 * d_v
+
+
+def query_output_bytes_per_head(d_qk: int = D_QK, d_v: int = D_V, elem_bytes: int = 2) -> int:
+    return elem_bytes * (d_qk + d_v)
+
+
+def kv_bytes_per_token(w: Workload) -> int:
+    """Bytes of one stored latent row: 576 bf16, or 576 e4m3 codes + one fp32 scale."""
+    return 2 * D_QK if w.kv_dtype == "bf16" else D_QK + 4
+
+
+def visible_scores(w: Workload, lens) -> int:
+    """Sum over requests and query rows of the positions each row attends to."""
+    tot = 0
+    for L in np.asarray(lens, dtype=np.int64):
+        for i in range(w.q_len):
+            vis = int(L) - w.q_len + i + 1 if w.causal else int(L)
+            tot += max(vis, 0) * w.H
+    return tot
+
+
+def layer_step(w: Workload, lens) -> dict:
+    """Algorithmic work of one layer-step of the whole emulated c-rank group."""
+    lens = np.asarray(lens, dtype=np.int64)
+    kv = int(lens.sum()) * kv_bytes_per_token(w)
+    flops = visible_scores(w, lens) * flops_per_score()
+    rows = w.B * w.q_len * w.H
+    q_bytes = rows * D_QK * 2
+    part_bytes = w.c * rows * (D_V + 1) * 4            # fp32 o_r and lse_r
+    final_bytes = rows * (D_V * 2 + 4)                 # bf16 o and fp32 lse
+    return dict(kv_bytes=kv, flops=flops, rows=rows, q_bytes=q_bytes,
+                partial_bytes=part_bytes, final_bytes=final_bytes,
+                decode_bytes=kv + w.c * q_bytes + part_bytes,
+                merge_bytes=part_bytes + final_bytes,
+                intensity=flops / kv if kv else 0.0)
