@@ -1,0 +1,218 @@
+/*
+ * dcp_mla.h - C ABI of the MI355X (gfx950) decode-context-parallel MLA hot path.
+ *
+ * Decode context parallelism (DCP) stripes one request's latent KV cache over a
+ * group of c ranks by token position: rank r owns the positions p with
+ * p mod c = r (SGLang documentation page "Decode Context Parallelism",
+ * introduction).  Each rank attends its own shard and returns a locally
+ * normalised output o_r with its log-sum-exp lse_r; the group merges the
+ * partials exactly (same page, section "MLA decode dataflow").
+ *
+ * One library instance serves either a real rank (rank_count = 1) or, on one
+ * GPU, an emulated group of c owner pools laid out back to back in HBM
+ * (rank_begin = 0, rank_count = c), with dcp_lse_merge standing in for the
+ * group's all-to-all.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named in the argument lists are DEVICE pointers unless marked
+ *   "host".  The caller owns every buffer; the library allocates and frees
+ *   nothing and keeps no state between calls (several streams may use it at
+ *   once on disjoint buffers).
+ * - Every call only enqueues work on `stream` (0 = the null stream) and never
+ *   synchronises.
+ * - A negative return value is a host-detected argument error: nothing was
+ *   enqueued and no buffer changed.  DCP_ERR_HIP reports a failed launch.
+ * - Errors that depend on device-resident values (lengths, page ids) are
+ *   reported by raising *dev_status (int32, device) to the largest
+ *   DCP_DEV_* code met; the caller clears it to 0 beforehand and reads it
+ *   when convenient.  dev_status may be NULL to skip the report.
+ * - bf16 values are raw 16-bit bfloat16 payloads.  The e4m3 KV format is OCP
+ *   FP8 E4M3FN codes with one float32 scale per token row
+ *   (value = decode(code) * scale).
+ * - Latent rows are DCP_D_QK = 576 wide: 512 latent columns then 64 rope
+ *   columns.  V is the first DCP_D_V = 512 columns of the same row (vLLM
+ *   GLM-5.3 blog post, section "Why the numbers add up": QK over 576
+ *   dimensions, PV over 512).
+ * - Pool layout: rank r's pool is [num_pages][page][row] with
+ *   row = 1152 bytes (bf16) or 576 bytes (e4m3); a pool's physical slot s is
+ *   row s.  The c pools sit back to back (pool r at pools + r*pool_bytes).
+ *   e4m3 scales live apart in float32 [c][num_pages*page].
+ * - Block table: int32 [batch][bt_stride]; entry g of request b is the page
+ *   id of its g-th virtual page.  The same table serves every rank (a
+ *   virtual page id indexes one physical page in every owner pool).
+ */
+#ifndef DCP_MLA_H
+#define DCP_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DCP_D_QK 576
+#define DCP_D_V 512
+#define DCP_MAX_Q_LEN 8
+
+/* Host-detected status (return values). */
+typedef enum dcp_status {
+  DCP_OK = 0,
+  DCP_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum value   */
+  DCP_ERR_UNSUPPORTED = -2, /* shape outside what the kernels implement      */
+  DCP_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned              */
+  DCP_ERR_WORKSPACE = -4,   /* workspace smaller than the size query returned */
+  DCP_ERR_HIP = -5          /* kernel launch failed                          */
+} dcp_status;
+
+/* Device-detected status, written to *dev_status (largest code wins). */
+enum {
+  DCP_DEV_OK = 0,
+  DCP_DEV_OUT_OF_PAGES = 1,   /* allocator: free stack too short            */
+  DCP_DEV_BAD_LENGTH = 2,     /* a length is negative, shrinks, or exceeds max_seq_len */
+  DCP_DEV_TABLE_OVERFLOW = 3, /* a position needs a block-table column >= bt_stride */
+  DCP_DEV_BAD_PAGE = 4        /* a block-table entry is outside [0, num_pages) */
+};
+
+enum { DCP_KV_BF16 = 0, DCP_KV_FP8_E4M3 = 1 };
+enum { DCP_LSE_BASE_E = 0, DCP_LSE_BASE_2 = 1 };
+
+/* Geometry of one DCP group's paged latent cache (host struct). */
+typedef struct dcp_layout {
+  int32_t c;         /* DCP group size, >= 1                                  */
+  int32_t page;      /* physical page size P in tokens, >= 1                  */
+  int32_t num_pages; /* physical pages per owner pool; capacity C = num_pages*page */
+  int32_t kv_dtype;  /* DCP_KV_BF16 or DCP_KV_FP8_E4M3                        */
+} dcp_layout;
+
+/* Bytes of one rank's pool (num_pages * page * row bytes). */
+int64_t dcp_pool_bytes(const dcp_layout* layout);
+
+/*
+ * dcp_alloc_virtual - grow requests in the shared virtual allocator.
+ *
+ * SGLang "Decode Context Parallelism", section "Virtual KV layout": the group
+ * exposes one virtual allocator of capacity C*c with virtual pages of P*c
+ * tokens; one virtual page maps to one physical page on every rank, so the
+ * ranks stay balanced to within one token.
+ *
+ * Request b grows from old_len[b] to new_len[b] tokens and needs
+ * ceil(new/(P*c)) - ceil(old/(P*c)) new virtual pages.  Pages are popped from
+ * the top of free_stack (the k-th page taken overall is
+ * free_stack[*free_top - 1 - k]) in (request, logical page) order and written
+ * to block_table[b][ceil(old/(P*c)) + i].  *free_top is decreased by the
+ * number taken.  All or nothing: on DCP_DEV_BAD_LENGTH (negative or shrinking
+ * length), DCP_DEV_TABLE_OVERFLOW (a request needs more than bt_stride
+ * pages) or DCP_DEV_OUT_OF_PAGES no entry and no *free_top changes.
+ *
+ *   free_stack   int32 [*free_top] page ids (read only)
+ *   free_top     int32 [1], read and updated
+ *   old_len, new_len  int32 [batch]
+ *   block_table  int32 [batch][bt_stride]; columns below ceil(old/(P*c)) untouched
+ * Runs one workgroup; batch <= 65536.
+ */
+int dcp_alloc_virtual(const dcp_layout* layout, const int32_t* free_stack, int32_t* free_top,
+                      const int32_t* old_len, const int32_t* new_len, int32_t batch,
+                      int32_t* block_table, int32_t bt_stride, int32_t* dev_status,
+                      hipStream_t stream);
+
+/*
+ * dcp_kv_write - scatter new latent rows into their owner pools.
+ *
+ * SGLang "Decode Context Parallelism", section "Virtual KV layout": every
+ * rank sees the same request-to-token map, keeps the positions it owns and
+ * compacts them into its physical pool.  Position p of request b has virtual
+ * slot v = block_table[b][p / (P*c)] * P*c + p mod (P*c); its owner is
+ * v mod c and its physical slot there is v / c.
+ *
+ * Request b appends rows cu_new[b] .. cu_new[b+1]-1 (n_b rows) at positions
+ * seq_len[b]-n_b .. seq_len[b]-1 (seq_len is the length after the append).
+ * Row bytes are copied unchanged (plus the e4m3 scale).  A row whose position
+ * is negative (DCP_DEV_BAD_LENGTH), whose table column is >= bt_stride
+ * (DCP_DEV_TABLE_OVERFLOW) or whose page id is outside [0, num_pages)
+ * (DCP_DEV_BAD_PAGE) is skipped and its slot_out is -1; other rows are
+ * written.  Slots not addressed keep their bytes.
+ *
+ *   pools        c pools (see layout above), written
+ *   pool_scales  float32 [c][num_pages*page] for e4m3, else NULL
+ *   seq_len      int32 [batch]; cu_new int32 [batch+1] with cu_new[batch] = n_rows
+ *   rows         [n_rows][576] bf16 payloads, or [n_rows][576] e4m3 codes
+ *   row_scales   float32 [n_rows] for e4m3, else NULL
+ *   slot_out     optional int64 [n_rows]: owner * (num_pages*page) + physical slot
+ */
+int dcp_kv_write(const dcp_layout* layout, void* pools, float* pool_scales,
+                 const int32_t* block_table, int32_t bt_stride, const int32_t* seq_len,
+                 const int32_t* cu_new, int32_t batch, int64_t n_rows, const void* rows,
+                 const float* row_scales, int64_t* slot_out, int32_t* dev_status,
+                 hipStream_t stream);
+
+/*
+ * mla_decode_workspace_size - bytes of workspace mla_decode_partial needs for
+ * these sizes (0 if none).  max_seq_len bounds every seq_len[b].
+ */
+size_t mla_decode_workspace_size(const dcp_layout* layout, int32_t rank_count, int32_t batch,
+                                 int32_t q_len, int32_t heads, int64_t max_seq_len);
+
+/*
+ * mla_decode_partial - absorbed-MLA decode attention of each rank over its own
+ * striped shard, returning the rank-local (o_r, lse_r).
+ *
+ * SGLang "Decode Context Parallelism", sections "MLA decode dataflow" and
+ * "DCP x speculative decoding": each rank attends only its owned positions
+ * through a rank-local page table built from owner(p) = p mod c and returns
+ * a locally normalised output with its LSE; for target verification the
+ * kernel is given the group size, the rank and the global KV length so that
+ * causality is judged on global positions.
+ *
+ * Rank r's j-th owned token is global position p = j*c + r and sits at
+ * physical slot block_table[b][j / P] * P + j mod P of pool r (the shared
+ * block table is the rank-local page table).  For query row (b, i, h), with
+ * i < q_len and global length L = seq_len[b], the visible positions are
+ * p <= L - q_len + i when causal, all p < L otherwise.  Scores are
+ * sm_scale * <q, K_p> over the 576 columns, (times the row's scale for e4m3);
+ * o_r = softmax-weighted sum of K_p[0:512]; lse_r = log of the sum of
+ * exp(scores) in the requested base.  A rank with no visible token returns
+ * o_r = 0 and lse_r = -inf.
+ *
+ *   pools, pool_scales  pool of rank rank_begin followed by the next
+ *                       rank_count-1 pools (a real rank passes its own pool
+ *                       with rank_count = 1)
+ *   q            bf16 [batch][q_len][heads][576]; heads % 16 == 0, q_len <= 8
+ *   seq_len      int32 [batch], 0 <= seq_len[b] <= max_seq_len (host value)
+ *   o_part       float32 [rank_count][batch][q_len][heads][512]
+ *   lse_part     float32 [rank_count][batch][q_len][heads]
+ *   workspace    device scratch of at least mla_decode_workspace_size(...)
+ *                bytes (may be NULL if that size is 0); contents are scratch
+ */
+int mla_decode_partial(const dcp_layout* layout, const void* pools, const float* pool_scales,
+                       int32_t rank_begin, int32_t rank_count, const void* q, int32_t batch,
+                       int32_t q_len, int32_t heads, const int32_t* block_table,
+                       int32_t bt_stride, const int32_t* seq_len, int64_t max_seq_len,
+                       float sm_scale, int32_t lse_base, int32_t causal, float* o_part,
+                       float* lse_part, void* workspace, size_t workspace_bytes,
+                       int32_t* dev_status, hipStream_t stream);
+
+/*
+ * dcp_lse_merge - exact merge of c partials (SGLang "Decode Context
+ * Parallelism", section "MLA decode dataflow"): lse = logsumexp_r lse_r and
+ * o = sum_r exp(lse_r - lse) * o_r, in base e or base 2 (the base of the
+ * partials).  Partials with lse_r = -inf get weight 0; if every partial of a
+ * row is -inf the row gets o = 0 and lse = -inf.
+ *
+ *   o_part   float32 [c][rows][512];  lse_part float32 [c][rows]
+ *   o_out    bf16 [rows][512], rounded to nearest even
+ *   lse_out  float32 [rows]
+ */
+int dcp_lse_merge(int32_t c, int64_t rows, const float* o_part, const float* lse_part,
+                  int32_t lse_base, void* o_out, float* lse_out, hipStream_t stream);
+
+/* Static description of a status value (host or device code). */
+const char* dcp_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCP_MLA_H */

@@ -1,0 +1,186 @@
+"""ctypes binding of libdcpmla.so: argument marshalling only.
+
+Every function here has the name of a C entry point in include/dcp_mla.h,
+checks that the torch tensors it is handed have the dtype, device and
+contiguity that entry point expects, and passes their device pointers and the
+current HIP stream through.  All computation happens in the HIP kernels; if
+the shared library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdcpmla.so")
+
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+LSE_BASE_E = 0
+LSE_BASE_2 = 1
+D_QK = 576
+D_V = 512
+MAX_Q_LEN = 8
+
+DEV_OK = 0
+DEV_OUT_OF_PAGES = 1
+DEV_BAD_LENGTH = 2
+DEV_TABLE_OVERFLOW = 3
+DEV_BAD_PAGE = 4
+
+
+class DcpError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status} ({text})")
+        self.status = status
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("c", ctypes.c_int32), ("page", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+    def __repr__(self):
+        return f"Layout(c={self.c}, page={self.page}, num_pages={self.num_pages}, kv_dtype={self.kv_dtype})"
+
+
+_lib = None
+_VP = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_PL = ctypes.POINTER(Layout)
+
+_SIGS = {
+    "dcp_pool_bytes": (_I64, [_PL]),
+    "dcp_alloc_virtual": (ctypes.c_int, [_PL, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _VP, _VP]),
+    "dcp_kv_write": (ctypes.c_int, [_PL, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I64, _VP, _VP, _VP, _VP, _VP]),
+    "mla_decode_workspace_size": (ctypes.c_size_t, [_PL, _I32, _I32, _I32, _I32, _I64]),
+    "mla_decode_partial": (ctypes.c_int, [_PL, _VP, _VP, _I32, _I32, _VP, _I32, _I32, _I32, _VP, _I32, _VP,
+                                          _I64, ctypes.c_float, _I32, _I32, _VP, _VP, _VP, ctypes.c_size_t,
+                                          _VP, _VP]),
+    "dcp_lse_merge": (ctypes.c_int, [_I32, _I64, _VP, _VP, _I32, _VP, _VP, _VP]),
+    "dcp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+def load_library(path: str = LIB_PATH):
+    """Load (once) and return the shared library; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it first (python -m kv_sharded_mla_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def dcp_status_string(status: int) -> str:
+    return load_library().dcp_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise DcpError(fn, status, dcp_status_string(status))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel=None) -> int:
+    if t is None:
+        return 0
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return int(t.data_ptr())
+
+
+def make_layout(c: int, page: int, num_pages: int, kv_dtype: int = KV_BF16) -> Layout:
+    return Layout(int(c), int(page), int(num_pages), int(kv_dtype))
+
+
+def dcp_pool_bytes(layout: Layout) -> int:
+    return int(load_library().dcp_pool_bytes(ctypes.byref(layout)))
+
+
+def dcp_alloc_virtual(layout: Layout, free_stack, free_top, old_len, new_len, block_table,
+                      dev_status=None, stream=None):
+    B = old_len.numel()
+    lib = load_library()
+    st = lib.dcp_alloc_virtual(
+        ctypes.byref(layout), _ptr(free_stack, "free_stack", torch.int32), _ptr(free_top, "free_top", torch.int32, 1),
+        _ptr(old_len, "old_len", torch.int32), _ptr(new_len, "new_len", torch.int32, B), B,
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[-1],
+        _ptr(dev_status, "dev_status", torch.int32, 1), _stream(stream))
+    _check("dcp_alloc_virtual", st)
+
+
+def dcp_kv_write(layout: Layout, pools, pool_scales, block_table, seq_len, cu_new, rows, row_scales=None,
+                 slot_out=None, dev_status=None, stream=None):
+    B = seq_len.numel()
+    n_rows = rows.shape[0]
+    lib = load_library()
+    st = lib.dcp_kv_write(
+        ctypes.byref(layout), _ptr(pools, "pools", (torch.uint8, torch.int16, torch.bfloat16)),
+        _ptr(pool_scales, "pool_scales", torch.float32), _ptr(block_table, "block_table", torch.int32),
+        block_table.shape[-1], _ptr(seq_len, "seq_len", torch.int32), _ptr(cu_new, "cu_new", torch.int32, B + 1),
+        B, n_rows, _ptr(rows, "rows", (torch.uint8, torch.int16, torch.bfloat16)),
+        _ptr(row_scales, "row_scales", torch.float32), _ptr(slot_out, "slot_out", torch.int64),
+        _ptr(dev_status, "dev_status", torch.int32, 1), _stream(stream))
+    _check("dcp_kv_write", st)
+
+
+def mla_decode_workspace_size(layout: Layout, rank_count: int, batch: int, q_len: int, heads: int,
+                              max_seq_len: int) -> int:
+    return int(load_library().mla_decode_workspace_size(ctypes.byref(layout), rank_count, batch, q_len, heads,
+                                                        int(max_seq_len)))
+
+
+def mla_decode_partial(layout: Layout, pools, pool_scales, rank_begin: int, rank_count: int, q, block_table,
+                       seq_len, max_seq_len: int, sm_scale: float, lse_base: int, causal: bool, o_part, lse_part,
+                       workspace=None, dev_status=None, stream=None):
+    """q: bf16 (or int16 payload) [batch][q_len][heads][576]."""
+    batch, q_len, heads, d = q.shape
+    if d != D_QK:
+        raise ValueError("q must be [batch][q_len][heads][576]")
+    rows = batch * q_len * heads
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    st = lib.mla_decode_partial(
+        ctypes.byref(layout), _ptr(pools, "pools", (torch.uint8, torch.int16, torch.bfloat16)),
+        _ptr(pool_scales, "pool_scales", torch.float32), rank_begin, rank_count,
+        _ptr(q, "q", (torch.bfloat16, torch.int16)), batch, q_len, heads,
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[-1],
+        _ptr(seq_len, "seq_len", torch.int32, batch), int(max_seq_len), float(sm_scale), int(lse_base),
+        1 if causal else 0, _ptr(o_part, "o_part", torch.float32, rank_count * rows * D_V),
+        _ptr(lse_part, "lse_part", torch.float32, rank_count * rows), _ptr(workspace, "workspace"), ws_bytes,
+        _ptr(dev_status, "dev_status", torch.int32, 1), _stream(stream))
+    _check("mla_decode_partial", st)
+
+
+def dcp_lse_merge(c: int, o_part, lse_part, lse_base: int, o_out, lse_out, stream=None):
+    rows = lse_out.numel()
+    lib = load_library()
+    st = lib.dcp_lse_merge(
+        int(c), rows, _ptr(o_part, "o_part", torch.float32, c * rows * D_V),
+        _ptr(lse_part, "lse_part", torch.float32, c * rows), int(lse_base),
+        _ptr(o_out, "o_out", (torch.bfloat16, torch.int16), rows * D_V), _ptr(lse_out, "lse_out", torch.float32),
+        _stream(stream))
+    _check("dcp_lse_merge", st)

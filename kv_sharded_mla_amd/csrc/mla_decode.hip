@@ -1,0 +1,509 @@
+// Paged split-KV absorbed-MLA decode over a DCP rank's striped shard (gfx950).
+//
+// Method (SGLang "Decode Context Parallelism", sections "MLA decode dataflow"
+// and "DCP x speculative decoding"): rank r attends only the positions it
+// owns, p = j*c + r, through a rank-local page table built from the cyclic
+// owner map, judges causality on global positions, and returns a locally
+// normalised output with its log-sum-exp.  Rank r's j-th token sits at slot
+// block_table[b][j / P] * P + j mod P of its pool, because floor((jc+r)/(Pc))
+// = floor(j/P) and floor(((jc+r) mod Pc)/c) = j mod P for r < c: the shared
+// block table is the rank-local page table.
+//
+// Kernel shape.  A workgroup of 4 waves owns one (rank, request, KV split,
+// block of 16*RG query rows).  KV is streamed through a 4-stage LDS ring filled
+// by direct-to-LDS 16-byte loads (global_load_lds_dwordx4); every latent row is
+// read from HBM once per workgroup and serves all of its query rows:
+//   S^T[32 tok x 16 rows] = K[32 x 576] . Q^T           (mfma 16x16x32 bf16, K from LDS,
+//                                                       Q^T held in registers)
+//   O^T[512 x 16 rows]   += V^T[512 x 32] . P^T         (V^T read from the same LDS rows
+//                                                       with ds_read_b64_tr_b16 / tr_b8)
+// The MFMA output layout of S^T (lane = 16g + j holds tokens 4g+i of row j)
+// is used directly as the P^T operand of the PV product by pairing k-slot
+// 8g+i with token 4g+i and k-slot 8g+4+i with token 16+4g+i; the transposed V
+// reads supply the same token order.  Every value a lane accumulates belongs
+// to its row j, so the softmax rescale is a per-lane scalar.
+// Waves split the 16*RG rows (RG groups) and, when RG < 4, the 512 output
+// columns (4/RG groups; each such wave recomputes the row's scores, which is
+// cheap for these HBM-bound shapes).
+// Online softmax runs in fp32 in base 2 (scores pre-multiplied by
+// sm_scale*log2 e); the running maximum is only raised when a tile exceeds it
+// by more than kTau, so O is rescaled rarely (any common reference value gives
+// the same result; probabilities stay below 2^kTau).
+// e4m3 KV: codes are converted exactly to bf16 for the MFMA, the per-token
+// scale multiplies the score and the probability that weights V.
+#include "dcp_common.hpp"
+#include "dcp_internal.hpp"
+
+#include "../../include/dcp_mla.h"
+
+namespace dcp {
+
+namespace {
+
+constexpr int kStages = 4;
+constexpr float kTau = 8.0f;
+constexpr int kMaxTab = 256;  // page ids staged per workgroup
+
+struct DecodeParams {
+  const uint8_t* pools;
+  const float* pool_scales;
+  int64_t pool_bytes;
+  int64_t cap;  // tokens per pool
+  int32_t c, page, num_pages, rank_begin;
+  const uint16_t* q;
+  int32_t batch, q_len, heads, rows;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const int32_t* seq_len;
+  int64_t max_seq_len;
+  float scale_log2;  // sm_scale * log2(e)
+  int32_t out_base2;  // lse written in base 2 (else base e)
+  int32_t causal;
+  float* o_out;    // [rank][batch][splits][rows][512]
+  float* lse_out;  // [rank][batch][splits][rows]
+  int32_t splits;
+  int64_t split_tokens;
+  int32_t n_row_blocks;
+  int64_t units_total;
+  int32_t* dev_status;
+};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+__device__ __forceinline__ bf16x8 cvt_fp8x8(i32x2 v) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[0], 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[0], 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[1], 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[1], 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ float wave_max_g(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_g(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+template <int RG, bool FP8, bool ALIGNED>
+__global__ void __launch_bounds__(256, 1) mla_decode_kernel(DecodeParams p) {
+  constexpr int DG = 4 / RG;              // column groups
+  constexpr int MB = 16 * RG;             // query rows per workgroup
+  constexpr int ROWB = FP8 ? kDqk : 2 * kDqk;
+  constexpr int CH = ROWB / 16;           // 16-byte chunks per latent row
+  constexpr int STOK = FP8 ? 64 : 32;     // tokens per stage
+  constexpr int NSUB = STOK / 32;
+  constexpr int SBYTES = STOK * ROWB;     // 36864 either way
+  constexpr int NI = SBYTES / 1024 / 4;   // 16-byte load instructions per wave per stage
+  constexpr int NVM = NI + (FP8 ? 1 : 0); // vector-memory ops per wave per stage
+  constexpr int NDB = 32 / DG;            // 16-column output blocks per wave
+  static_assert(SBYTES % 4096 == 0, "stage must split evenly over 4 waves");
+
+  // Four distinct stage arrays (not one indexed ring): with every stage named
+  // statically the compiler can tell that LDS reads of one stage do not alias
+  // the direct-to-LDS loads in flight into the others, and inserts no
+  // vector-memory waits before those reads.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv0[SBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv1[SBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv2[SBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv3[SBYTES];
+  __shared__ __attribute__((aligned(16))) float lds_sc0[FP8 ? STOK : 4];
+  __shared__ __attribute__((aligned(16))) float lds_sc1[FP8 ? STOK : 4];
+  __shared__ __attribute__((aligned(16))) float lds_sc2[FP8 ? STOK : 4];
+  __shared__ __attribute__((aligned(16))) float lds_sc3[FP8 ? STOK : 4];
+  static_assert(kStages == 4, "the ring below is unrolled for four stages");
+  __shared__ int32_t lds_pt[kMaxTab];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, j = lane & 15;
+  const int rg = w / DG, dg = w % DG;
+
+  // XCD-aware unit mapping: the row blocks of one (rank, request, split) sit on
+  // the same XCD (ids congruent mod 8) so their KV reads share that L2.
+  const int64_t id = blockIdx.x;
+  const int xcd = (int)(id & 7);
+  const int64_t qq = id >> 3;
+  const int rb = (int)(qq % p.n_row_blocks);
+  const int64_t unit = (qq / p.n_row_blocks) * 8 + xcd;
+  if (unit >= p.units_total) return;
+  const int split = (int)(unit % p.splits);
+  const int64_t rbu = unit / p.splits;
+  const int b = (int)(rbu % p.batch);
+  const int rl = (int)(rbu / p.batch);
+  const int64_t r = (int64_t)p.rank_begin + rl;
+  const int64_t c = p.c, P = p.page;
+
+  const int row0 = rb * MB + rg * 16;     // first query row of this wave
+  const int64_t orow = (((int64_t)rl * p.batch + b) * p.splits + split) * p.rows + row0 + j;
+
+  int32_t L = p.seq_len[b];
+  bool ok = true;
+  if (L < 0 || (int64_t)L > p.max_seq_len) {
+    if (tid == 0 && p.dev_status) atomicMax(p.dev_status, DCP_DEV_BAD_LENGTH);
+    ok = false;
+  } else if (((int64_t)L + P * c - 1) / (P * c) > p.bt_stride) {
+    if (tid == 0 && p.dev_status) atomicMax(p.dev_status, DCP_DEV_TABLE_OVERFLOW);
+    ok = false;
+  }
+  if (!ok) L = 0;
+
+  // all rank-local token indices fit in int32 (seq_len is int32)
+  const int32_t ri = (int32_t)r, ci32 = (int32_t)c, Pi = (int32_t)P;
+  const int32_t n_r = L > ri ? (L - ri + ci32 - 1) / ci32 : 0;
+  auto visible = [&](int qi) -> int32_t {  // rank-local tokens visible to query index qi
+    int32_t lim = p.causal ? L - p.q_len + qi : L - 1;
+    if (lim < ri) return 0;
+    int32_t n = (lim - ri) / ci32 + 1;
+    return n < n_r ? n : n_r;
+  };
+  const int32_t split_tok = (int32_t)p.split_tokens;
+  const int32_t j_begin = split * split_tok;
+  const int32_t n_wg = visible((rb * MB + MB - 1) / p.heads);
+  const int32_t j_end = min(n_wg, j_begin + split_tok);
+  const int32_t jlim = min(visible(row0 / p.heads), j_begin + split_tok);
+  const int n_st = j_end > j_begin ? (j_end - j_begin + STOK - 1) / STOK : 0;
+
+  const uint8_t* pool = p.pools + (int64_t)rl * p.pool_bytes;
+  const float* spool = FP8 ? p.pool_scales + (int64_t)rl * p.cap : nullptr;
+  const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
+
+  // Page ids of this split, staged once in LDS so that the load pipeline below
+  // never waits on a vector-memory result.  Invalid ids are reported and
+  // replaced by page 0 so that every access stays inside the pool.
+  const int32_t vp_first = j_begin / Pi;
+  const int32_t n_tab = n_st > 0 ? (j_end - 1) / Pi - vp_first + 1 : 0;  // <= kMaxTab by the plan
+  {
+    bool bad_page = false;
+    for (int t = tid; t < n_tab; t += 256) {
+      int32_t pg = bt[vp_first + t];
+      if ((unsigned)pg >= (unsigned)p.num_pages) {
+        bad_page = true;
+        pg = 0;
+      }
+      lds_pt[t] = pg;
+    }
+    if (bad_page && p.dev_status) atomicMax(p.dev_status, DCP_DEV_BAD_PAGE);
+  }
+
+  // Q^T operand for this wave's 16 rows: lane (g, j) holds q[row0+j][32kk+8g .. +8].
+  bf16x8 qf[18];
+  {
+    const uint16_t* qrow = p.q + ((int64_t)b * p.rows + row0 + j) * kDqk + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk);
+  }
+  __syncthreads();  // page table visible; Q landed
+
+  const int32_t jb_off = j_begin - vp_first * Pi;  // offset of j_begin inside its page
+  auto issue = [&](int s, uint8_t* dst, float* dst_sc) {
+    const int32_t j0 = j_begin + s * STOK;
+    // aligned: the stage lies inside one page (P is a multiple of STOK and so is j_begin)
+    int32_t al_pg = 0, al_off = 0;
+    if (ALIGNED) {
+      const int32_t rel = jb_off + s * STOK;
+      const int32_t pidx = rel / Pi;
+      al_pg = lds_pt[pidx];
+      al_off = rel - pidx * Pi;
+    }
+    auto slot = [&](int32_t jj) -> int64_t {
+      if (ALIGNED) return (int64_t)al_pg * Pi + al_off + (jj - j0);
+      const int32_t pidx = jj / Pi;
+      return (int64_t)lds_pt[pidx - vp_first] * Pi + (jj - pidx * Pi);
+    };
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const int qi = w + 4 * t;
+      const int ci = qi * 64 + lane;
+      const int row = ci / CH, col = ci % CH;
+      const int32_t jj = min(j0 + row, j_end - 1);
+      const uint8_t* src = pool + slot(jj) * ROWB + col * 16;
+      __builtin_amdgcn_global_load_lds((const void*)src, DCP_LDS(void, dst + qi * 1024), 16, 0, 0);
+    }
+    if (FP8) {
+      const int32_t jj = min(j0 + 16 * w + (lane & 15), j_end - 1);
+      const float* src = spool + slot(jj);
+      if (lane < 16)
+        __builtin_amdgcn_global_load_lds((const void*)src, DCP_LDS(void, dst_sc + 16 * w), 4, 0, 0);
+    }
+  };
+
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // per-lane LDS offsets of the transposed V reads
+  const int tr_row16 = 4 * (lane >> 4) + ((lane >> 2) & 3);       // bf16: + 16*half
+  const int tr_col16 = 8 * (lane & 3);                             // bytes within a 32-byte column block
+  const int s8 = (lane & 15) >> 1;
+  const int tr_row8 = s8 < 4 ? 4 * (lane >> 4) + s8 : 16 + 4 * (lane >> 4) + (s8 - 4);
+  const int tr_col8 = 8 * (lane & 1);
+
+  // One ring step: wait for stage s, refill the stage computed one step ago,
+  // then compute stage s.
+  auto step = [&](int s, const uint8_t* kv, const float* sc, uint8_t* refill, float* refill_sc) {
+    const int ahead = min(kStages - 2, n_st - 1 - s);
+    if (ahead >= 2) wait_vmcnt<2 * NVM>();
+    else if (ahead == 1) wait_vmcnt<NVM>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (s + kStages - 1 < n_st) issue(s + kStages - 1, refill, refill_sc);
+    const int32_t j0 = j_begin + s * STOK;
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const int tb0 = sub * 32;
+      const int32_t jt = j0 + tb0;
+      if (jt >= jlim) break;  // nothing visible to this wave's rows from here on
+      // ---- scores: S^T = K . Q^T for two 16-token blocks
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const int rowk = tb0 + tb * 16 + j;
+          bf16x8 a;
+          if (FP8) {
+            i32x2 raw = *reinterpret_cast<const i32x2*>(kv + rowk * ROWB + 32 * kk + 8 * g);
+            a = cvt_fp8x8(raw);
+          } else {
+            a = *reinterpret_cast<const bf16x8*>(kv + rowk * ROWB + 64 * kk + 16 * g);
+          }
+          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sacc[tb], 0, 0, 0);
+        }
+      }
+      // ---- online softmax (base 2), lane holds tokens tb*16 + 4g + i of row j
+      float sv[8], tsc[8];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tb * 16 + 4 * g + i;
+          float x = sacc[tb][i] * p.scale_log2;
+          if (FP8) {
+            tsc[tb * 4 + i] = sc[tb0 + t];
+            x *= tsc[tb * 4 + i];
+          }
+          x = (jt + t < jlim) ? x : -INFINITY;
+          sv[tb * 4 + i] = x;
+          mt = fmaxf(mt, x);
+        }
+      }
+      mt = wave_max_g(mt);
+      float alpha = 1.f;
+      if (mt > m_run + kTau) {  // also true when m_run is -inf and the tile has a visible token
+        alpha = exp2f(m_run - mt);
+        m_run = mt;
+      }
+      const float mref = m_run == -INFINITY ? 0.f : m_run;
+      float psum = 0.f;
+      bf16x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float pe = exp2f(sv[e] - mref);
+        psum += pe;
+        if (FP8) pe *= tsc[e];
+        pf[e] = (__bf16)pe;
+      }
+      l_run = l_run * alpha + psum;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) acc[d] *= alpha;
+      }
+      // ---- O^T += V^T . P^T over this 32-token sub-tile
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        const int db = dg * NDB + d;
+        bf16x8 a;
+        if (FP8) {
+          i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              DCP_LDS(i32x2, kv + (tb0 + tr_row8) * ROWB + db * 16 + tr_col8));
+          a = cvt_fp8x8(raw);
+        } else {
+          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              DCP_LDS(i16x4, kv + (tb0 + tr_row16) * ROWB + db * 32 + tr_col16));
+          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              DCP_LDS(i16x4, kv + (tb0 + 16 + tr_row16) * ROWB + db * 32 + tr_col16));
+          typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+          i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          a = __builtin_bit_cast(bf16x8, v);
+        }
+        acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, acc[d], 0, 0, 0);
+      }
+    }
+  };
+
+  if (n_st > 0) issue(0, lds_kv0, lds_sc0);
+  if (n_st > 1) issue(1, lds_kv1, lds_sc1);
+  if (n_st > 2) issue(2, lds_kv2, lds_sc2);
+  for (int s = 0; s < n_st; s += kStages) {
+    step(s, lds_kv0, lds_sc0, lds_kv3, lds_sc3);
+    if (s + 1 >= n_st) break;
+    step(s + 1, lds_kv1, lds_sc1, lds_kv0, lds_sc0);
+    if (s + 2 >= n_st) break;
+    step(s + 2, lds_kv2, lds_sc2, lds_kv1, lds_sc1);
+    if (s + 3 >= n_st) break;
+    step(s + 3, lds_kv3, lds_sc3, lds_kv2, lds_sc2);
+  }
+
+  // ---- finalise: o = O / l, lse = m + log2(l) (then base conversion)
+  const float l_tot = wave_sum_g(l_run);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  float* orow_ptr = p.o_out + orow * kDv;
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+    const int col = (dg * NDB + d) * 16 + 4 * g;
+    *reinterpret_cast<f32x4*>(orow_ptr + col) = acc[d] * inv;
+  }
+  if (dg == 0 && g == 0) {
+    float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+    p.lse_out[orow] = p.out_base2 ? lse2 : lse2 * kLn2;
+  }
+}
+
+// Merge the KV splits of every (rank, request, row): ws [units][splits][rows] -> o_part, lse_part.
+__global__ void __launch_bounds__(256)
+split_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int32_t splits,
+                     int32_t rows, int64_t n_rows_total, int32_t out_base2, float* __restrict__ o_part,
+                     float* __restrict__ lse_part) {
+  const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+  const int col4 = threadIdx.x & 127;
+  if (row >= n_rows_total) return;
+  const int64_t unit = row / rows, rr = row % rows;
+  const float* o = ws_o + (unit * splits * rows + rr) * kDv;
+  const float* l = ws_lse + unit * splits * rows + rr;
+  f32x4 acc;
+  float lse2;
+  merge_row4(o, (int64_t)rows * kDv, l, rows, splits, true, col4, acc, lse2);
+  *reinterpret_cast<f32x4*>(o_part + row * kDv + 4 * col4) = acc;
+  if (col4 == 0) lse_part[row] = out_base2 ? lse2 : lse2 * kLn2;
+}
+
+template <int RG, bool FP8, bool ALIGNED>
+hipError_t launch_variant(const DecodeParams& prm, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((mla_decode_kernel<RG, FP8, ALIGNED>), dim3((unsigned)grid), dim3(256), 0, stream, prm);
+  return hipGetLastError();
+}
+
+template <int RG, bool FP8>
+hipError_t launch_rg(const DecodeParams& prm, bool aligned, int64_t grid, hipStream_t s) {
+  return aligned ? launch_variant<RG, FP8, true>(prm, grid, s) : launch_variant<RG, FP8, false>(prm, grid, s);
+}
+
+}  // namespace
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+DecodePlan plan_decode(int32_t c, int32_t page, bool fp8, int32_t rank_count, int32_t batch, int32_t q_len,
+                       int32_t heads, int64_t max_seq_len) {
+  DecodePlan pl{};
+  pl.rows = q_len * heads;
+  const int rg = pl.rows % 64 == 0 ? 4 : (pl.rows % 32 == 0 ? 2 : 1);
+  pl.row_block = 16 * rg;
+  pl.n_row_blocks = pl.rows / pl.row_block;
+  pl.stage_tokens = fp8 ? 64 : 32;
+  const int64_t n_r_max = (max_seq_len + c - 1) / c;
+  const int64_t stages_max = (n_r_max + pl.stage_tokens - 1) / pl.stage_tokens;
+  const int64_t units = (int64_t)rank_count * batch * pl.n_row_blocks;
+  const int64_t target = 2 * (int64_t)device_cu_count();
+  int64_t splits = units > 0 ? (target + units - 1) / units : 1;
+  // a split's page ids must fit the workgroup's LDS table of kMaxTab entries
+  int64_t max_split_tokens = fp8 ? 8192 : 4096;
+  const int64_t tab_tokens = (int64_t)(kMaxTab - 1) * page / pl.stage_tokens * pl.stage_tokens;
+  if (tab_tokens < max_split_tokens) max_split_tokens = tab_tokens;
+  splits = std::max<int64_t>(splits, (n_r_max + max_split_tokens - 1) / max_split_tokens);
+  // at least 4 stages per split, unless the page table bound asks for more splits
+  splits = std::min<int64_t>(splits, std::max<int64_t>((stages_max + 3) / 4,
+                                                       (n_r_max + max_split_tokens - 1) / max_split_tokens));
+  if (splits < 1) splits = 1;
+  int64_t per = stages_max > 0 ? (stages_max + splits - 1) / splits : 1;
+  if (per * pl.stage_tokens > max_split_tokens) per = max_split_tokens / pl.stage_tokens;
+  splits = stages_max > 0 ? (stages_max + per - 1) / per : 1;
+  pl.splits = (int32_t)splits;
+  pl.split_tokens = per * pl.stage_tokens;
+  pl.workspace_bytes =
+      splits > 1 ? (size_t)rank_count * batch * splits * pl.rows * (kDv + 1) * sizeof(float) : 0;
+  return pl;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {
+  if (a.batch == 0 || a.rank_count == 0) return hipSuccess;
+  DecodeParams prm{};
+  const int row_bytes = a.fp8 ? kDqk : 2 * kDqk;
+  prm.pools = (const uint8_t*)a.pools;
+  prm.pool_scales = a.pool_scales;
+  prm.cap = (int64_t)a.num_pages * a.page;
+  prm.pool_bytes = prm.cap * row_bytes;
+  prm.c = a.c;
+  prm.page = a.page;
+  prm.num_pages = a.num_pages;
+  prm.rank_begin = a.rank_begin;
+  prm.q = (const uint16_t*)a.q;
+  prm.batch = a.batch;
+  prm.q_len = a.q_len;
+  prm.heads = a.heads;
+  prm.rows = pl.rows;
+  prm.block_table = a.block_table;
+  prm.bt_stride = a.bt_stride;
+  prm.seq_len = a.seq_len;
+  prm.max_seq_len = a.max_seq_len;
+  prm.scale_log2 = a.sm_scale * kLog2e;
+  prm.causal = a.causal ? 1 : 0;
+  prm.splits = pl.splits;
+  prm.split_tokens = pl.split_tokens;
+  prm.n_row_blocks = pl.n_row_blocks;
+  prm.units_total = (int64_t)a.rank_count * a.batch * pl.splits;
+  prm.dev_status = a.dev_status;
+  float* ws_o = nullptr;
+  float* ws_lse = nullptr;
+  if (pl.splits > 1) {
+    ws_o = (float*)a.workspace;
+    ws_lse = ws_o + (size_t)a.rank_count * a.batch * pl.splits * pl.rows * kDv;
+    prm.o_out = ws_o;
+    prm.lse_out = ws_lse;
+    prm.out_base2 = 1;
+  } else {
+    prm.o_out = a.o_part;
+    prm.lse_out = a.lse_part;
+    prm.out_base2 = a.base2 ? 1 : 0;
+  }
+  const bool aligned = a.page % pl.stage_tokens == 0;
+  const int64_t grid = (prm.units_total + 7) / 8 * 8 * pl.n_row_blocks;
+  hipError_t e;
+  const int rg = pl.row_block / 16;
+  if (a.fp8) {
+    e = rg == 4 ? launch_rg<4, true>(prm, aligned, grid, stream)
+                : rg == 2 ? launch_rg<2, true>(prm, aligned, grid, stream) : launch_rg<1, true>(prm, aligned, grid, stream);
+  } else {
+    e = rg == 4 ? launch_rg<4, false>(prm, aligned, grid, stream)
+                : rg == 2 ? launch_rg<2, false>(prm, aligned, grid, stream) : launch_rg<1, false>(prm, aligned, grid, stream);
+  }
+  if (e != hipSuccess || pl.splits == 1) return e;
+  const int64_t n_rows_total = (int64_t)a.rank_count * a.batch * pl.rows;
+  hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)((n_rows_total + 1) / 2)), dim3(256), 0, stream, ws_o,
+                     ws_lse, pl.splits, pl.rows, n_rows_total, a.base2 ? 1 : 0, a.o_part, a.lse_part);
+  return hipGetLastError();
+}
+
+}  // namespace dcp

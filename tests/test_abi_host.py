@@ -1,0 +1,103 @@
+"""Host-side checks of the C ABI (CPU only, no kernel launches).
+
+The shared library must load, export every function that include/dcp_mla.h
+declares, and reject bad arguments on the host with the documented negative
+status before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dcp_mla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from kv_sharded_mla_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        from kv_sharded_mla_amd.build import build
+        build()
+    return _binding.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b((?:dcp|mla)_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"dcp_alloc_virtual", "dcp_kv_write", "mla_decode_partial", "dcp_lse_merge",
+            "mla_decode_workspace_size", "dcp_status_string", "dcp_pool_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    from kv_sharded_mla_amd import dcp_status_string
+    assert dcp_status_string(0) == "ok"
+    assert "out of pages" in dcp_status_string(1)
+    assert "aligned" in dcp_status_string(-3)
+    assert dcp_status_string(12345) == "unknown status"
+
+
+def _layout(c=4, page=16, num_pages=10, kv=0):
+    from kv_sharded_mla_amd import make_layout
+    return make_layout(c, page, num_pages, kv)
+
+
+def test_pool_bytes(lib):
+    from kv_sharded_mla_amd import dcp_pool_bytes
+    assert dcp_pool_bytes(_layout(4, 16, 10, 0)) == 10 * 16 * 1152
+    assert dcp_pool_bytes(_layout(4, 16, 10, 1)) == 10 * 16 * 576
+    assert dcp_pool_bytes(_layout(0, 16, 10, 0)) == -1
+    assert dcp_pool_bytes(_layout(4, 16, 10, 7)) == -1
+
+
+def test_host_argument_errors(lib):
+    L = _layout()
+    ref = ctypes.byref(L)
+    # merge: bad c, bad base, null pointers, misalignment
+    assert lib.dcp_lse_merge(0, 4, 16, 16, 0, 16, 16, None) == -1
+    assert lib.dcp_lse_merge(2, 4, 16, 16, 5, 16, 16, None) == -1
+    assert lib.dcp_lse_merge(2, 4, None, 16, 0, 16, 16, None) == -1
+    assert lib.dcp_lse_merge(2, 4, 8, 16, 0, 16, 16, None) == -3
+    assert lib.dcp_lse_merge(2, 0, None, None, 0, None, None, None) == 0   # nothing to do
+    # decode: unsupported heads / q_len, bad rank range, missing workspace
+    args = dict(pools=16, scales=None, rb=0, rc=4, q=16, B=1, q_len=1, H=16, bt=16, bts=4, sl=16, maxl=64,
+                scale=0.1, base=0, causal=1, o=16, lse=16, ws=None, wsb=0, st=None, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.mla_decode_partial(ref, a["pools"], a["scales"], a["rb"], a["rc"], a["q"], a["B"], a["q_len"],
+                                      a["H"], a["bt"], a["bts"], a["sl"], a["maxl"], a["scale"], a["base"],
+                                      a["causal"], a["o"], a["lse"], a["ws"], a["wsb"], a["st"], a["stream"])
+    assert call(H=24) == -2
+    assert call(q_len=9) == -2
+    assert call(rb=2, rc=3) == -1
+    assert call(scale=float("inf")) == -1
+    assert call(q=8) == -3
+    assert call(base=3) == -1
+    assert call(maxl=2**31) == -2
+    assert call(B=0) == 0
+    # a long context needs split workspace: none given
+    assert call(maxl=1 << 20, B=1) == -4
+    # kv write / alloc
+    assert lib.dcp_kv_write(ref, 16, None, 16, 4, 16, 16, 1, 4, 8, None, None, None, None) == -3
+    assert lib.dcp_kv_write(ctypes.byref(_layout(kv=1)), 16, None, 16, 4, 16, 16, 1, 4, 16, None, None, None,
+                            None) == -1
+    assert lib.dcp_alloc_virtual(ref, 16, None, 16, 16, 1, 16, 4, None, None) == -1
+    assert lib.dcp_alloc_virtual(ref, 16, 16, 16, 16, -1, 16, 4, None, None) == -1
+
+
+def test_workspace_size_matches_split_plan(lib):
+    from kv_sharded_mla_amd import mla_decode_workspace_size
+    # short contexts need no split workspace; a 1M-token fp8 context does
+    assert mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 64, 1, 16, 32768) == 0
+    n = mla_decode_workspace_size(_layout(8, 64, 100, 1), 8, 4, 1, 64, 1 << 20)
+    assert n > 0 and n % (4 * 513) == 0
+    assert mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 4, 9, 64, 1000) == 0  # invalid -> 0
