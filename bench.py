@@ -1,0 +1,266 @@
+"""Benchmark of the DCP MLA decode hot path on one MI355X.
+
+One step = one layer-step of an emulated c-rank DCP group: allocate virtual
+pages for the q_len new tokens of every request, scatter their latent rows
+into the owner pools, attend every rank's striped shard (partials), and merge
+the partials.  The context (L - q_len tokens per request) is written before
+timing and stays resident in HBM; two identical copies of the pools are used
+in alternation so consecutive steps never find the previous step's KV in the
+256 MB MALL.
+
+Prints one JSON line (rank 0).  Progress goes to stderr.
+
+    python bench.py [--config tplocal] [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("mla_decode.hip", "dcp_common.hpp"):
+        with open(os.path.join(ROOT, "kv_sharded_mla_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(cfg_name: str):
+    """HBM traffic per decode launch from a committed counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", f"mla_decode_{cfg_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, lens, budget_s: float):
+    """The oracle as it stands (rank partials + merge), timed on a sample of requests."""
+    import numpy as np
+    from oracle import attention as OA
+    from workloads import accounting, gen
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = os.cpu_count() or 1
+    q_bits = gen.q_bits(w)
+    done_bytes = 0
+    t_total = 0.0
+    n = 0
+    for b in range(w.B):
+        L = int(lens[b])
+        kv = gen.kv_rows(w, b, L)           # stored-format bytes (generation not timed)
+        t0 = time.perf_counter()
+        op, lp = OA.rank_partials(q_bits[b], kv, L, w.sm_scale, w.c, w.causal, w.lse_base)
+        OA.merge(op, lp, w.lse_base)
+        t_total += time.perf_counter() - t0
+        done_bytes += L * accounting.kv_bytes_per_token(w)
+        n += 1
+        if t_total >= budget_s:
+            break
+    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"requests 0..{n - 1} of {w.name} ({n}/{w.B}), all {w.H} heads x q_len {w.q_len}, "
+                      f"{w.c} rank partials + merge in float64, {t_total:.1f} s",
+            "seconds": round(t_total, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="tplocal")
+    ap.add_argument("--copies", type=int, default=2, help="pool copies used in rotation")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", type=int, default=0,
+                    help="after the timed steps, launch the decode entry point this many more times (profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; the c-rank DCP group is emulated on that GPU "
+              "(--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_sharded_mla_amd as K
+    from kv_sharded_mla_amd.group import DcpGroup
+    from workloads import accounting, configs, gen
+
+    w = configs.BY_NAME[args.config]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lens = gen.lengths(w)
+    ctx = np.maximum(lens - w.q_len, 0)           # resident context before the step's new tokens
+    num_pages = gen.pool_pages(w, lens)
+    vp = w.P * w.c
+    stride = int(max((int(L) + vp - 1) // vp for L in lens))
+    kv_kind = K.KV_FP8_E4M3 if w.kv_dtype == "fp8" else K.KV_BF16
+    base = K.LSE_BASE_2 if w.lse_base == "2" else K.LSE_BASE_E
+
+    log(f"workload {w.name}: B={w.B} H={w.H} q_len={w.q_len} c={w.c} P={w.P} kv={w.kv_dtype} "
+        f"sum(L)={int(lens.sum())}; generating inputs")
+    t0 = time.time()
+    data, scale, cu = gen.batch_rows(w, lens)
+    log(f"generated {data.nbytes / 2**30:.2f} GiB of latent rows in {time.time() - t0:.1f} s")
+    # split every request's rows into resident context and the step's new rows
+    ctx_idx = np.concatenate([np.arange(cu[b], cu[b] + ctx[b]) for b in range(w.B)]).astype(np.int64)
+    new_idx = np.concatenate([np.arange(cu[b] + ctx[b], cu[b + 1]) for b in range(w.B)]).astype(np.int64)
+    row_u8 = data.view(np.uint8).reshape(len(data), -1)
+    new_rows = torch.from_numpy(row_u8[new_idx]).to(dev)
+    new_sc = torch.from_numpy(scale[new_idx]).to(dev) if scale is not None else None
+    stack = gen.free_stack(w, num_pages)
+    groups = []
+    ctx_rows = torch.from_numpy(row_u8[ctx_idx]).to(dev)
+    ctx_sc = torch.from_numpy(scale[ctx_idx]).to(dev) if scale is not None else None
+    del data, scale, row_u8
+    for k in range(args.copies):
+        g = DcpGroup(w.c, w.P, num_pages, kv_kind, w.B, stride, free_stack=stack, device="cuda:0")
+        g.append([int(x) for x in ctx], ctx_rows, ctx_sc)
+        groups.append(g)
+    del ctx_rows, ctx_sc
+    torch.cuda.synchronize()
+    assert all(g.status() == 0 for g in groups)
+    log(f"{args.copies} resident pool copies written ({groups[0].pools.numel() * args.copies / 2**30:.2f} GiB)")
+
+    q = torch.from_numpy(gen.q_bits(w).view(np.int16)).to(dev)
+    old_len = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+    new_len = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    cu_new = torch.from_numpy(np.concatenate([[0], np.cumsum(lens - ctx)]).astype(np.int32)).to(dev)
+    max_len = int(lens.max())
+    for g in groups:
+        g.max_seq_len = max_len
+    ws_bytes = K.mla_decode_workspace_size(groups[0].layout, w.c, w.B, w.q_len, w.H, max_len)
+    ws = torch.empty(max(ws_bytes // 4, 4), dtype=torch.float32, device=dev) if ws_bytes else None
+    o_part = torch.empty((w.c, w.B, w.q_len, w.H, K.D_V), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((w.c, w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
+    o = torch.empty((w.B, w.q_len, w.H, K.D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    # If a new token opens a virtual page, every step pops the same pages again from the
+    # same stack top: restore the top first so repeated steps stay identical.
+    need_pages = int(sum((int(L) + vp - 1) // vp - (int(x) + vp - 1) // vp for L, x in zip(lens, ctx)))
+    saved_top = [g.free_top.clone() for g in groups]
+
+    def step(g, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        if need_pages:
+            g.free_top.copy_(saved_top[groups.index(g)])
+        K.dcp_alloc_virtual(g.layout, g.free_stack, g.free_top, old_len, new_len, g.block_table, g.dev_status)
+        K.dcp_kv_write(g.layout, g.pools, g.pool_scales, g.block_table, new_len, cu_new, new_rows, new_sc, None,
+                       g.dev_status)
+        if ev is not None:
+            ev[1].record(stream)
+        K.mla_decode_partial(g.layout, g.pools, g.pool_scales, 0, w.c, q, g.block_table, new_len, max_len,
+                             w.sm_scale, base, w.causal, o_part, lse_part, ws, g.dev_status)
+        if ev is not None:
+            ev[2].record(stream)
+        K.dcp_lse_merge(w.c, o_part, lse_part, base, o, lse)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(groups[i % len(groups)])
+    torch.cuda.synchronize()
+    assert all(g.status() == 0 for g in groups), [g.status() for g in groups]
+    for g in groups:
+        g.seq_len = new_len.clone()
+    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(groups[i % len(groups)], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    assert all(g.status() == 0 for g in groups), [g.status() for g in groups]
+    t_write = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    t_merge = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    t_step = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"per step: wall {ms_per_step * 1e3:.1f} us; events: write {t_write * 1e3:.1f} us, decode "
+        f"{t_dec * 1e3:.1f} us, merge {t_merge * 1e3:.1f} us, step {t_step * 1e3:.1f} us")
+    for i in range(args.decode_only):
+        g = groups[i % len(groups)]
+        K.mla_decode_partial(g.layout, g.pools, g.pool_scales, 0, w.c, q, g.block_table, new_len, max_len,
+                             w.sm_scale, base, w.causal, o_part, lse_part, ws, g.dev_status)
+    torch.cuda.synchronize()
+
+    acct = accounting.layer_step(w, lens)
+    kv_gbps = acct["kv_bytes"] / (ms_per_step * 1e-3) / 1e9
+    tflops = acct["flops"] / (ms_per_step * 1e-3) / 1e12
+    dec_gbps = acct["decode_bytes"] / (t_dec * 1e-3) / 1e9
+    dec_tflops = acct["flops"] / (t_dec * 1e-3) / 1e12
+    mfma_bound = w.H * w.q_len >= 128
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dec_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4)}
+    roof["traffic"] = load_traffic(w.name)
+    roof["kernel"] = "mla_decode_partial (mla_decode_kernel + split combine when splits > 1)"
+    roof["algorithmic_bytes_per_launch"] = acct["decode_bytes"]
+    roof["flops_per_launch"] = acct["flops"]
+    roof["hbm_frac"] = round(dec_gbps / HBM_PEAK_GBPS, 4)
+    roof["mfma_frac"] = round(dec_tflops / MFMA_BF16_PEAK_TFLOPS, 4)
+    roof["launch_us"] = round(t_dec * 1e3, 2)
+
+    out = {
+        "metric": "DCP MLA decode: achieved KV GB/s & % roofline; TFLOP/s; us per layer-step",
+        "value": round(kv_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q and latent KV" + (", e4m3 + fp32 per-token scale" if w.kv_dtype == "fp8"
+                                                              else ", bf16") + ")",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "q_len": w.q_len, "dcp": w.c, "page": w.P,
+                   "kv": w.kv_dtype, "context_tokens": int(lens.sum()), "max_len": max_len,
+                   "lse_base": w.lse_base, "emulated_ranks_on_one_gpu": w.c},
+        "us_per_layer_step": round(ms_per_step * 1e3, 2),
+        "tflops": round(tflops, 2),
+        "kernel_us": {"alloc+kv_write": round(t_write * 1e3, 2), "mla_decode_partial": round(t_dec * 1e3, 2),
+                      "dcp_lse_merge": round(t_merge * 1e3, 2)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the oracle on the host for about {args.cpu_budget:.0f} s")
+        out["cpu_baseline"] = cpu_baseline(w, lens, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

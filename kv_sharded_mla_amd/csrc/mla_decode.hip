@@ -41,8 +41,18 @@ namespace dcp {
 namespace {
 
 constexpr int kStages = 4;
+constexpr int kWaves = 8;     // waves per workgroup: two per SIMD
+constexpr int kThreads = kWaves * 64;
 constexpr float kTau = 8.0f;
-constexpr int kMaxTab = 256;  // page ids staged per workgroup
+constexpr int kMaxTab = 256;
+#ifndef DCP_SCHED_K
+#define DCP_SCHED_K 6
+#endif
+#ifndef DCP_SCHED_V
+#define DCP_SCHED_V 4
+#endif
+constexpr int kSchedK = DCP_SCHED_K;  // k units per scheduling window
+constexpr int kSchedV = DCP_SCHED_V;  // output blocks per scheduling window  // page ids staged per workgroup
 
 struct DecodeParams {
   const uint8_t* pools;
@@ -68,11 +78,59 @@ struct DecodeParams {
   int32_t* dev_status;
 };
 
+// LDS layout of a stage: row r (token) of ROWB bytes holds its 16-byte chunk c
+// at position c ^ swz(r).  The XOR stays inside aligned groups of 8 (bf16,
+// 72 chunks per row) or 4 (e4m3, 36 chunks) so it permutes each row.  Without
+// it the 1152- and 576-byte row strides put the 16 rows that one LDS read
+// instruction touches on the same banks.
+#ifndef DCP_LDS_SWIZZLE
+#define DCP_LDS_SWIZZLE 1
+#endif
+template <bool FP8>
+__device__ __forceinline__ int swz(int r) {
+  if (FP8) return ((r >> 1) & 3) ^ ((r >> 3) & 3);
+#if DCP_LDS_SWIZZLE == 0
+  return 2 * (((r >> 1) ^ r) & 3) + ((r >> 2) & 1);  // no conflicts with 32 banks of 4 bytes
+#else
+  return ((r >> 1) ^ r) & 7;                           // no conflicts with 64 banks of 4 bytes
+#endif
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Direct-to-LDS loads: every active lane k of the wave copies 16 (or 4) bytes
+// from its global address to LDS byte lds + 16k (or 4k); lds must be
+// wave-uniform.  Written as inline asm so that the compiler's wait-count
+// insertion does not treat the ring's later LDS reads as aliasing these
+// writes.  m0 carries the LDS address; nothing else in these kernels uses m0
+// (a host-side build check verifies this in the generated code).
+__device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(gbase)
+                   : "memory");
+}
+__device__ __forceinline__ void dma16_abs(const uint8_t* gaddr, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gaddr) : "memory");
+}
+__device__ __forceinline__ void dma4_abs(const float* gaddr, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(gaddr) : "memory");
+}
+
+// Workgroup barrier without the release fence of __syncthreads (which would
+// wait for every direct-to-LDS load in flight).  The empty asm statements keep
+// the compiler from moving memory accesses across it; LDS writes that other
+// waves read after it are completed first with an explicit lgkmcnt(0).
+__device__ __forceinline__ void wg_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ bf16x8 cvt_fp8x8(i32x2 v) {
@@ -96,38 +154,39 @@ __device__ __forceinline__ float wave_sum_g(float v) {
 }
 
 template <int RG, bool FP8, bool ALIGNED>
-__global__ void __launch_bounds__(256, 1) mla_decode_kernel(DecodeParams p) {
-  constexpr int DG = 4 / RG;              // column groups
+__global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p) {
+  constexpr int SUB = kWaves / RG;        // waves per row group
+  constexpr int NKP = SUB / 2;            // k-parts of the score product per token block
   constexpr int MB = 16 * RG;             // query rows per workgroup
   constexpr int ROWB = FP8 ? kDqk : 2 * kDqk;
   constexpr int CH = ROWB / 16;           // 16-byte chunks per latent row
   constexpr int STOK = FP8 ? 64 : 32;     // tokens per stage
-  constexpr int NSUB = STOK / 32;
+  constexpr int NSUB = STOK / 32;         // 32-token sub-tiles per stage
   constexpr int SBYTES = STOK * ROWB;     // 36864 either way
-  constexpr int NI = SBYTES / 1024 / 4;   // 16-byte load instructions per wave per stage
-  constexpr int NVM = NI + (FP8 ? 1 : 0); // vector-memory ops per wave per stage
-  constexpr int NDB = 32 / DG;            // 16-column output blocks per wave
-  static_assert(SBYTES % 4096 == 0, "stage must split evenly over 4 waves");
+  constexpr int NI_ALL = SBYTES / 1024;   // 1 KB direct-to-LDS loads per stage
+  constexpr int NI_MAX = (NI_ALL + kWaves - 1) / kWaves;
+  constexpr int NDB = 32 / SUB;           // 16-column output blocks per wave
+  constexpr int KU = FP8 ? 9 : 18;        // k units: bf16 k-steps, or e4m3 k-step pairs
+  constexpr int KUW = (KU + NKP - 1) / NKP;  // most k units one wave handles
+  constexpr int NQF = FP8 ? 2 * KUW : KUW;   // Q^T fragments held by a wave
+  static_assert(RG == 1 || RG == 2 || RG == 4, "row groups");
+  static_assert(NI_ALL % 4 == 0 && NI_ALL / kWaves + 1 == NI_MAX, "load split");
 
-  // Four distinct stage arrays (not one indexed ring): with every stage named
-  // statically the compiler can tell that LDS reads of one stage do not alias
-  // the direct-to-LDS loads in flight into the others, and inserts no
-  // vector-memory waits before those reads.
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv0[SBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv1[SBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv2[SBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv3[SBYTES];
-  __shared__ __attribute__((aligned(16))) float lds_sc0[FP8 ? STOK : 4];
-  __shared__ __attribute__((aligned(16))) float lds_sc1[FP8 ? STOK : 4];
-  __shared__ __attribute__((aligned(16))) float lds_sc2[FP8 ? STOK : 4];
-  __shared__ __attribute__((aligned(16))) float lds_sc3[FP8 ? STOK : 4];
-  static_assert(kStages == 4, "the ring below is unrolled for four stages");
+  // Stage ring.  The direct-to-LDS loads that fill it are issued from inline
+  // asm (dma_* below), so the compiler does not see them as pending LDS
+  // writes and inserts no vector-memory waits before the ring's LDS reads;
+  // the explicit vmcnt waits and barriers in step() order them instead.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv[kStages * SBYTES];
+  __shared__ __attribute__((aligned(16))) float lds_sc[FP8 ? kStages * STOK : 4];
+  __shared__ __attribute__((aligned(16))) f32x4 lds_xch[kWaves * 64];  // partial S^T blocks
   __shared__ int32_t lds_pt[kMaxTab];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, j = lane & 15;
-  const int rg = w / DG, dg = w % DG;
+  const int rg = w / SUB, sw = w % SUB;
+  const int tb = sw & 1, kp = sw >> 1;      // score slice: token block, k part
+  const int ku0 = KU * kp / NKP, nku = KU * (kp + 1) / NKP - ku0;
 
   // XCD-aware unit mapping: the row blocks of one (rank, request, split) sit on
   // the same XCD (ids congruent mod 8) so their KV reads share that L2.
@@ -144,7 +203,7 @@ __global__ void __launch_bounds__(256, 1) mla_decode_kernel(DecodeParams p) {
   const int64_t r = (int64_t)p.rank_begin + rl;
   const int64_t c = p.c, P = p.page;
 
-  const int row0 = rb * MB + rg * 16;     // first query row of this wave
+  const int row0 = rb * MB + rg * 16;     // first query row of this wave's row group
   const int64_t orow = (((int64_t)rl * p.batch + b) * p.splits + split) * p.rows + row0 + j;
 
   int32_t L = p.seq_len[b];
@@ -185,7 +244,7 @@ __global__ void __launch_bounds__(256, 1) mla_decode_kernel(DecodeParams p) {
   const int32_t n_tab = n_st > 0 ? (j_end - 1) / Pi - vp_first + 1 : 0;  // <= kMaxTab by the plan
   {
     bool bad_page = false;
-    for (int t = tid; t < n_tab; t += 256) {
+    for (int t = tid; t < n_tab; t += kThreads) {
       int32_t pg = bt[vp_first + t];
       if ((unsigned)pg >= (unsigned)p.num_pages) {
         bad_page = true;
@@ -196,165 +255,243 @@ __global__ void __launch_bounds__(256, 1) mla_decode_kernel(DecodeParams p) {
     if (bad_page && p.dev_status) atomicMax(p.dev_status, DCP_DEV_BAD_PAGE);
   }
 
-  // Q^T operand for this wave's 16 rows: lane (g, j) holds q[row0+j][32kk+8g .. +8].
-  bf16x8 qf[18];
+  // Q^T operand of this wave's score slice (rows row0..row0+15, k units
+  // [ku0, ku0+nku)).  bf16: unit u is k-step u and lane (g, j) holds
+  // q[row0+j][32u+8g .. +8].  e4m3: unit u is the k-step pair read with one
+  // 16-byte K load, fragment 2i+e holds q[row0+j][64u+16g+8e .. +8]; any order
+  // of the 576 columns gives the same dot product when K and Q agree.
+  bf16x8 qf[NQF];
   {
-    const uint16_t* qrow = p.q + ((int64_t)b * p.rows + row0 + j) * kDqk + 8 * g;
+    const uint16_t* qrow = p.q + ((int64_t)b * p.rows + row0 + j) * kDqk;
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk);
+    for (int i = 0; i < KUW; ++i) {
+      const int u = min(ku0 + i, KU - 1);
+      if (FP8) {
+        qf[2 * i] = *reinterpret_cast<const bf16x8*>(qrow + 64 * u + 16 * g);
+        qf[2 * i + 1] = *reinterpret_cast<const bf16x8*>(qrow + 64 * u + 16 * g + 8);
+      } else {
+        qf[i] = *reinterpret_cast<const bf16x8*>(qrow + 32 * u + 8 * g);
+      }
+    }
   }
-  __syncthreads();  // page table visible; Q landed
+  // Q (and the page table) must have landed before the loop: the compiler
+  // does not count the asm loads below, so a wait for Q placed inside the
+  // loop would also drain every load in flight.
+  wait_vmcnt<0>();
+  __syncthreads();  // page table visible
 
+  // ---- direct-to-LDS loads of one stage.  Wave w issues loads w, w+8, ... of
+  // the stage's NI_ALL; load i fills LDS bytes [1024 i, 1024 i + 1024), lane k
+  // the 16 bytes at 1024 i + 16 k, which hold chunk (pos ^ swz(row)) of stage
+  // row `row` (pos = position inside the row).
+  const int ni = (w < NI_ALL % kWaves) ? NI_MAX : NI_MAX - 1;  // loads this wave issues
+  int dma_row[NI_MAX];        // stage row (token) each load of this lane fetches
+  uint32_t dma_off[NI_MAX];   // its byte offset from the stage's first row
+#pragma unroll
+  for (int t = 0; t < NI_MAX; ++t) {
+    const int ci = (w + kWaves * t) * 64 + lane;
+    const int row = min(ci / CH, STOK - 1);
+    dma_row[t] = row;
+    dma_off[t] = (uint32_t)(row * ROWB + ((ci % CH) ^ swz<FP8>(row)) * 16);
+  }
   const int32_t jb_off = j_begin - vp_first * Pi;  // offset of j_begin inside its page
-  auto issue = [&](int s, uint8_t* dst, float* dst_sc) {
+  auto slot_of = [&](int32_t jj) -> int64_t {
+    const int32_t pidx = jj / Pi;
+    return (int64_t)lds_pt[pidx - vp_first] * Pi + (jj - pidx * Pi);
+  };
+  auto issue = [&](int s) {
+    uint8_t* dst = lds_kv + (s % kStages) * SBYTES;
+    float* dst_sc = lds_sc + (FP8 ? (s % kStages) * STOK : 0);
     const int32_t j0 = j_begin + s * STOK;
-    // aligned: the stage lies inside one page (P is a multiple of STOK and so is j_begin)
-    int32_t al_pg = 0, al_off = 0;
-    if (ALIGNED) {
+    if (ALIGNED && j0 + STOK <= j_end) {
+      // whole stage inside one page: one page id, fixed per-lane offsets
       const int32_t rel = jb_off + s * STOK;
       const int32_t pidx = rel / Pi;
-      al_pg = lds_pt[pidx];
-      al_off = rel - pidx * Pi;
-    }
-    auto slot = [&](int32_t jj) -> int64_t {
-      if (ALIGNED) return (int64_t)al_pg * Pi + al_off + (jj - j0);
-      const int32_t pidx = jj / Pi;
-      return (int64_t)lds_pt[pidx - vp_first] * Pi + (jj - pidx * Pi);
-    };
+      const int32_t pg = __builtin_amdgcn_readfirstlane(lds_pt[pidx]);
+      const int64_t slot0 = (int64_t)pg * Pi + (rel - pidx * Pi);
+      const uint8_t* base = pool + slot0 * ROWB;
 #pragma unroll
-    for (int t = 0; t < NI; ++t) {
-      const int qi = w + 4 * t;
-      const int ci = qi * 64 + lane;
-      const int row = ci / CH, col = ci % CH;
-      const int32_t jj = min(j0 + row, j_end - 1);
-      const uint8_t* src = pool + slot(jj) * ROWB + col * 16;
-      __builtin_amdgcn_global_load_lds((const void*)src, DCP_LDS(void, dst + qi * 1024), 16, 0, 0);
-    }
-    if (FP8) {
-      const int32_t jj = min(j0 + 16 * w + (lane & 15), j_end - 1);
-      const float* src = spool + slot(jj);
-      if (lane < 16)
-        __builtin_amdgcn_global_load_lds((const void*)src, DCP_LDS(void, dst_sc + 16 * w), 4, 0, 0);
+      for (int t = 0; t < NI_MAX; ++t)
+        if (t < ni) dma16(base, dma_off[t], dst + (w + kWaves * t) * 1024);
+      if (FP8 && lane < 8) dma4_abs(spool + slot0 + 8 * w + lane, dst_sc + 8 * w);
+    } else {
+      // last stage of a split (rows past j_end repeat the last valid row) or
+      // pages that a stage can straddle
+#pragma unroll
+      for (int t = 0; t < NI_MAX; ++t)
+        if (t < ni) {
+          const int32_t jj = min(j0 + dma_row[t], j_end - 1);
+          dma16_abs(pool + slot_of(jj) * ROWB + (dma_off[t] - dma_row[t] * ROWB), dst + (w + kWaves * t) * 1024);
+        }
+      if (FP8) {
+        const int32_t jj = min(j0 + 8 * w + (lane & 7), j_end - 1);
+        const float* src = spool + slot_of(jj);
+        if (lane < 8) dma4_abs(src, dst_sc + 8 * w);
+      }
     }
   };
+
+  // Per-lane LDS byte offsets (swizzled) of the K and transposed-V reads.
+  // K (A operand of S^T): row 16*tb + j (+32*sub for e4m3), 16-byte chunk
+  // 4*u + g.
+  // bf16 V^T: ds_read_b64_tr_b16 lane k reads row 16*h + 4*(k>>4) + ((k>>2)&3),
+  // 8 bytes at column block db: chunk 2*db + ((k&3)>>1), half k&1.
+  // e4m3 V^T: ds_read_b64_tr_b8 lane k = 16G + 2s + q reads row tok(G, s) with
+  // tok = 4G+s (s<4) or 16+4G+s-4, chunk db, half q.
+  int koff[2], voff[2][4];
+  if (!FP8) {
+    // k-step u of row `row` sits at byte row*ROWB + 128*(u>>1) + 16*((4*(u&1)+g) ^ swz(row)):
+    // koff[e] is the offset of the wave's k-step ku0+e, and k-step ku0+e+2t lies 128*t further
+    const int row = 16 * tb + j;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int u = ku0 + e;
+      koff[e] = row * ROWB + 128 * (u >> 1) + 16 * ((4 * (u & 1) + g) ^ swz<false>(row));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int vrow = 16 * h + 4 * (lane >> 4) + ((lane >> 2) & 3);
+      const int y = ((lane & 3) >> 1) ^ swz<false>(vrow);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) voff[h][m] = vrow * ROWB + 16 * ((2 * m) ^ y) + 8 * (lane & 1);
+    }
+  } else {
+    const int s8 = (lane & 15) >> 1;
+    const int trow = s8 < 4 ? 4 * (lane >> 4) + s8 : 16 + 4 * (lane >> 4) + (s8 - 4);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int row = 32 * sub + 16 * tb + j;
+      koff[sub] = row * ROWB + 64 * ku0 + 16 * (g ^ swz<true>(row));
+      const int vrow = 32 * sub + trow;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) voff[sub][m] = vrow * ROWB + 16 * (m ^ swz<true>(vrow)) + 8 * (lane & 1);
+    }
+  }
 
   f32x4 acc[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  f32x4* xch_mine = lds_xch + w * 64 + lane;
+  const f32x4* xch_grp = lds_xch + rg * SUB * 64 + lane;
 
-  // per-lane LDS offsets of the transposed V reads
-  const int tr_row16 = 4 * (lane >> 4) + ((lane >> 2) & 3);       // bf16: + 16*half
-  const int tr_col16 = 8 * (lane & 3);                             // bytes within a 32-byte column block
-  const int s8 = (lane & 15) >> 1;
-  const int tr_row8 = s8 < 4 ? 4 * (lane >> 4) + s8 : 16 + 4 * (lane >> 4) + (s8 - 4);
-  const int tr_col8 = 8 * (lane & 1);
-
-  // One ring step: wait for stage s, refill the stage computed one step ago,
-  // then compute stage s.
-  auto step = [&](int s, const uint8_t* kv, const float* sc, uint8_t* refill, float* refill_sc) {
-    const int ahead = min(kStages - 2, n_st - 1 - s);
-    if (ahead >= 2) wait_vmcnt<2 * NVM>();
-    else if (ahead == 1) wait_vmcnt<NVM>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (s + kStages - 1 < n_st) issue(s + kStages - 1, refill, refill_sc);
-    const int32_t j0 = j_begin + s * STOK;
+  // One 32-token sub-tile of a resident stage.
+  auto tile = [&](const uint8_t* kv, const float* sc, int sub, int32_t jt) {
+    // ---- this wave's slice of S^T: token block tb, k units [ku0, ku0+nku)
+    f32x4 sp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-      const int tb0 = sub * 32;
-      const int32_t jt = j0 + tb0;
-      if (jt >= jlim) break;  // nothing visible to this wave's rows from here on
-      // ---- scores: S^T = K . Q^T for two 16-token blocks
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) {
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const int rowk = tb0 + tb * 16 + j;
-          bf16x8 a;
-          if (FP8) {
-            i32x2 raw = *reinterpret_cast<const i32x2*>(kv + rowk * ROWB + 32 * kk + 8 * g);
-            a = cvt_fp8x8(raw);
-          } else {
-            a = *reinterpret_cast<const bf16x8*>(kv + rowk * ROWB + 64 * kk + 16 * g);
-          }
-          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sacc[tb], 0, 0, 0);
-        }
-      }
-      // ---- online softmax (base 2), lane holds tokens tb*16 + 4g + i of row j
-      float sv[8], tsc[8];
-      float mt = -INFINITY;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = tb * 16 + 4 * g + i;
-          float x = sacc[tb][i] * p.scale_log2;
-          if (FP8) {
-            tsc[tb * 4 + i] = sc[tb0 + t];
-            x *= tsc[tb * 4 + i];
-          }
-          x = (jt + t < jlim) ? x : -INFINITY;
-          sv[tb * 4 + i] = x;
-          mt = fmaxf(mt, x);
-        }
-      }
-      mt = wave_max_g(mt);
-      float alpha = 1.f;
-      if (mt > m_run + kTau) {  // also true when m_run is -inf and the tile has a visible token
-        alpha = exp2f(m_run - mt);
-        m_run = mt;
-      }
-      const float mref = m_run == -INFINITY ? 0.f : m_run;
-      float psum = 0.f;
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float pe = exp2f(sv[e] - mref);
-        psum += pe;
-        if (FP8) pe *= tsc[e];
-        pf[e] = (__bf16)pe;
-      }
-      l_run = l_run * alpha + psum;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) acc[d] *= alpha;
-      }
-      // ---- O^T += V^T . P^T over this 32-token sub-tile
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        const int db = dg * NDB + d;
-        bf16x8 a;
+    for (int i = 0; i < KUW; ++i) {
+      // bound how far the scheduler hoists K loads ahead of their MFMAs
+      if (i % kSchedK == 0 && i > 0) __builtin_amdgcn_sched_barrier(0);
+      if (i < nku) {
+        const int u = ku0 + i;
         if (FP8) {
-          i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              DCP_LDS(i32x2, kv + (tb0 + tr_row8) * ROWB + db * 16 + tr_col8));
-          a = cvt_fp8x8(raw);
+          const i32x4 raw = *reinterpret_cast<const i32x4*>(kv + koff[sub] + 64 * i);
+          sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{raw[0], raw[1]}), qf[2 * i], sp, 0, 0, 0);
+          sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{raw[2], raw[3]}), qf[2 * i + 1], sp, 0, 0, 0);
         } else {
-          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              DCP_LDS(i16x4, kv + (tb0 + tr_row16) * ROWB + db * 32 + tr_col16));
-          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              DCP_LDS(i16x4, kv + (tb0 + 16 + tr_row16) * ROWB + db * 32 + tr_col16));
-          typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
-          i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          a = __builtin_bit_cast(bf16x8, v);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kv + koff[i & 1] + 128 * (i >> 1));
+          sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i], sp, 0, 0, 0);
         }
-        acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, acc[d], 0, 0, 0);
       }
+    }
+    // ---- exchange the slices of the row group; sum the k parts
+    *xch_mine = sp;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slice is in LDS
+    wg_barrier();
+    f32x4 sacc[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      sacc[t2] = xch_grp[t2 * 64];
+#pragma unroll
+      for (int k2 = 1; k2 < NKP; ++k2) sacc[t2] += xch_grp[(t2 + 2 * k2) * 64];
+    }
+    // ---- online softmax (base 2), lane holds tokens tb*16 + 4g + i of row j
+    const int tb0 = 32 * sub;
+    float sv[8], tsc[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t2 * 16 + 4 * g + i;
+        float x = sacc[t2][i] * p.scale_log2;
+        if (FP8) {
+          tsc[t2 * 4 + i] = sc[tb0 + t];
+          x *= tsc[t2 * 4 + i];
+        }
+        x = (jt + t < jlim) ? x : -INFINITY;
+        sv[t2 * 4 + i] = x;
+        mt = fmaxf(mt, x);
+      }
+    }
+    mt = wave_max_g(mt);
+    float alpha = 1.f;
+    if (mt > m_run + kTau) {  // also true when m_run is -inf and the tile has a visible token
+      alpha = exp2f(m_run - mt);
+      m_run = mt;
+    }
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
+    bf16x8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float pe = exp2f(sv[e] - mref);
+      psum += pe;
+      if (FP8) pe *= tsc[e];
+      pf[e] = (__bf16)pe;
+    }
+    l_run = l_run * alpha + psum;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) acc[d] *= alpha;
+    }
+    // ---- O^T += V^T . P^T for this wave's output columns
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      if (d % kSchedV == 0 && d > 0) __builtin_amdgcn_sched_barrier(0);
+      const int db = sw * NDB + d;
+      bf16x8 a;
+      if (FP8) {
+        i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(DCP_LDS(i32x2, kv + voff[sub][db & 3] + 64 * (db >> 2)));
+        a = cvt_fp8x8(raw);
+      } else {
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DCP_LDS(i16x4, kv + voff[0][db & 3] + 128 * (db >> 2)));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DCP_LDS(i16x4, kv + voff[1][db & 3] + 128 * (db >> 2)));
+        typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+        i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        a = __builtin_bit_cast(bf16x8, v);
+      }
+      acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, acc[d], 0, 0, 0);
     }
   };
 
-  if (n_st > 0) issue(0, lds_kv0, lds_sc0);
-  if (n_st > 1) issue(1, lds_kv1, lds_sc1);
-  if (n_st > 2) issue(2, lds_kv2, lds_sc2);
-  for (int s = 0; s < n_st; s += kStages) {
-    step(s, lds_kv0, lds_sc0, lds_kv3, lds_sc3);
-    if (s + 1 >= n_st) break;
-    step(s + 1, lds_kv1, lds_sc1, lds_kv0, lds_sc0);
-    if (s + 2 >= n_st) break;
-    step(s + 2, lds_kv2, lds_sc2, lds_kv1, lds_sc1);
-    if (s + 3 >= n_st) break;
-    step(s + 3, lds_kv3, lds_sc3, lds_kv2, lds_sc2);
+  // One ring step: wait for stage s, refill the stage computed one step ago,
+  // then compute stage s.  Barriers are uniform across the workgroup.
+  for (int s = 0; s < kStages - 1 && s < n_st; ++s) issue(s);
+  for (int s = 0; s < n_st; ++s) {
+    const int ahead = min(kStages - 2, n_st - 1 - s);
+    if (w < NI_ALL % kWaves) {
+      constexpr int NV = NI_MAX + (FP8 ? 1 : 0);
+      if (ahead >= 2) wait_vmcnt<2 * NV>();
+      else if (ahead == 1) wait_vmcnt<NV>();
+      else wait_vmcnt<0>();
+    } else {
+      constexpr int NV = NI_MAX - 1 + (FP8 ? 1 : 0);
+      if (ahead >= 2) wait_vmcnt<2 * NV>();
+      else if (ahead == 1) wait_vmcnt<NV>();
+      else wait_vmcnt<0>();
+    }
+    wg_barrier();
+    if (s + kStages - 1 < n_st) issue(s + kStages - 1);
+    const uint8_t* kv = lds_kv + (s % kStages) * SBYTES;
+    const float* sc = lds_sc + (FP8 ? (s % kStages) * STOK : 0);
+    const int32_t j0 = j_begin + s * STOK;
+    tile(kv, sc, 0, j0);
+    if (NSUB == 2 && j0 + 32 < j_end) {
+      wg_barrier();  // every wave has read the exchanged slices
+      tile(kv, sc, 1, j0 + 32);
+    }
   }
 
   // ---- finalise: o = O / l, lse = m + log2(l) (then base conversion)
@@ -363,10 +500,10 @@ __global__ void __launch_bounds__(256, 1) mla_decode_kernel(DecodeParams p) {
   float* orow_ptr = p.o_out + orow * kDv;
 #pragma unroll
   for (int d = 0; d < NDB; ++d) {
-    const int col = (dg * NDB + d) * 16 + 4 * g;
+    const int col = (sw * NDB + d) * 16 + 4 * g;
     *reinterpret_cast<f32x4*>(orow_ptr + col) = acc[d] * inv;
   }
-  if (dg == 0 && g == 0) {
+  if (sw == 0 && g == 0) {
     float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
     p.lse_out[orow] = p.out_base2 ? lse2 : lse2 * kLn2;
   }
@@ -392,7 +529,7 @@ split_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ w
 
 template <int RG, bool FP8, bool ALIGNED>
 hipError_t launch_variant(const DecodeParams& prm, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_decode_kernel<RG, FP8, ALIGNED>), dim3((unsigned)grid), dim3(256), 0, stream, prm);
+  hipLaunchKernelGGL((mla_decode_kernel<RG, FP8, ALIGNED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, prm);
   return hipGetLastError();
 }
 

@@ -1,0 +1,56 @@
+"""Static checks on the generated gfx950 code of the decode kernels (CPU only).
+
+The direct-to-LDS loads are issued from inline asm that sets m0 itself; that
+is only sound if nothing else in the kernels keeps a value in m0.  The
+kernels must also not spill (scratch traffic would add vector-memory
+operations that the hand-placed wait counts do not account for).
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "kv_sharded_mla_amd", "csrc", "mla_decode.hip")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    from kv_sharded_mla_amd.build import FLAGS, HIPCC
+    out = tmp_path_factory.mktemp("asm") / "mla_decode.s"
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "-S", "--cuda-device-only", SRC, "-o", str(out)]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout[-3000:]
+    return out.read_text()
+
+
+def _kernels(asm):
+    parts = re.split(r"\n(_ZN3dcp\w*mla_decode_kernel\w*):[^\n]*\n", asm)
+    return {parts[i]: parts[i + 1].split("s_endpgm")[0] for i in range(1, len(parts) - 1, 2)}
+
+
+def test_m0_only_feeds_lds_dma(asm):
+    lines = [l.strip() for l in asm.splitlines()]
+    code = [l for l in lines if l and not l.startswith((";", "."))]
+    uses = [i for i, l in enumerate(code) if re.search(r"\bm0\b", l.split(";")[0])]
+    assert uses, "expected the LDS-DMA m0 writes"
+    for i in uses:
+        ins = code[i].split(";")[0]
+        assert re.match(r"s_mov_b32 m0, s\d+$", ins), ins
+        assert code[i + 1].startswith("global_load_lds_dword"), code[i + 1]
+
+
+def test_decode_kernels_do_not_spill(asm):
+    ks = _kernels(asm)
+    assert len(ks) == 12
+    for name, body in ks.items():
+        assert "scratch_" not in body, name
+
+
+def test_no_compiler_vmcnt_waits_inside_decode_loop(asm):
+    # every vmcnt wait of the decode kernels is one of the explicit ones: the page table
+    # and Q loads before the loop (0), and the ring waits (0, one or two stages of loads)
+    for name, body in _kernels(asm).items():
+        waits = sorted(set(int(x) for x in re.findall(r"vmcnt\((\d+)\)", body)))
+        assert set(waits) <= {0, 4, 5, 6, 8, 10, 12}, (name, waits)
