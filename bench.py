@@ -92,6 +92,8 @@ def main():
     ap.add_argument("--copies", type=int, default=2, help="pool copies used in rotation")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB once (HBM counter calibration)")
     ap.add_argument("--decode-only", type=int, default=0,
                     help="after the timed steps, launch the decode entry point this many more times (profiling)")
     args = ap.parse_args()
@@ -209,6 +211,13 @@ def main():
         g = groups[i % len(groups)]
         K.mla_decode_partial(g.layout, g.pools, g.pool_scales, 0, w.c, q, g.block_table, new_len, max_len,
                              w.sm_scale, base, w.causal, o_part, lse_part, ws, g.dev_status)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
 
     acct = accounting.layer_step(w, lens)

@@ -44,15 +44,11 @@ constexpr int kStages = 4;
 constexpr int kWaves = 8;     // waves per workgroup: two per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr float kTau = 8.0f;
-constexpr int kMaxTab = 256;
+constexpr int kMaxTab = 256;  // page ids staged per workgroup
 #ifndef DCP_SCHED_K
 #define DCP_SCHED_K 6
 #endif
-#ifndef DCP_SCHED_V
-#define DCP_SCHED_V 4
-#endif
 constexpr int kSchedK = DCP_SCHED_K;  // k units per scheduling window
-constexpr int kSchedV = DCP_SCHED_V;  // output blocks per scheduling window  // page ids staged per workgroup
 
 struct DecodeParams {
   const uint8_t* pools;
@@ -133,6 +129,28 @@ __device__ __forceinline__ void wg_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
+// Wait until at most `ahead` (<= A) stages of this wave's loads, NV each, are
+// outstanding.
+template <int NV, int A>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  if constexpr (A == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= A) {
+      wait_vmcnt<A * NV>();
+      return;
+    }
+    wait_stages<NV, A - 1>(ahead);
+  }
+}
+// Waves below NBIG issue NI loads per stage, the others NI-1; e4m3 adds one
+// scale load per wave.
+template <int NI, int NBIG, bool FP8, int MAXA>
+__device__ __forceinline__ void wait_vmcnt_ahead(int w, int ahead) {
+  if (w < NBIG) wait_stages<NI + (FP8 ? 1 : 0), MAXA>(ahead);
+  else wait_stages<NI - 1 + (FP8 ? 1 : 0), MAXA>(ahead);
+}
+
 __device__ __forceinline__ bf16x8 cvt_fp8x8(i32x2 v) {
   bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[0], 1.0f, false);
   bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[0], 1.0f, true);
@@ -165,7 +183,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p)
   constexpr int SBYTES = STOK * ROWB;     // 36864 either way
   constexpr int NI_ALL = SBYTES / 1024;   // 1 KB direct-to-LDS loads per stage
   constexpr int NI_MAX = (NI_ALL + kWaves - 1) / kWaves;
-  constexpr int NDB = 32 / SUB;           // 16-column output blocks per wave
+  constexpr int NDB = 32 / kWaves;        // 16-column output blocks per wave (all row groups)
   constexpr int KU = FP8 ? 9 : 18;        // k units: bf16 k-steps, or e4m3 k-step pairs
   constexpr int KUW = (KU + NKP - 1) / NKP;  // most k units one wave handles
   constexpr int NQF = FP8 ? 2 * KUW : KUW;   // Q^T fragments held by a wave
@@ -180,6 +198,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p)
   __shared__ __attribute__((aligned(16))) float lds_sc[FP8 ? kStages * STOK : 4];
   __shared__ __attribute__((aligned(16))) f32x4 lds_xch[kWaves * 64];  // partial S^T blocks
   __shared__ int32_t lds_pt[kMaxTab];
+  __shared__ __attribute__((aligned(16))) bf16x8 lds_p[RG * 64];  // P^T operand of each row group
+  __shared__ float lds_alpha[RG * 16];                           // rescale factor per row
+  __shared__ float lds_l[RG * 16];                               // final normaliser per row
+  __shared__ int lds_resc[RG];                                   // tile whose P needs a rescale
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -368,12 +390,18 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p)
     }
   }
 
-  f32x4 acc[NDB];
+  // O^T accumulators: this wave's NDB output blocks for every row group.
+  f32x4 acc[NDB][RG];
 #pragma unroll
-  for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int q = 0; q < RG; ++q) acc[d][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // softmax state of row row0 + j (every wave of a row group keeps identical copies)
   float m_run = -INFINITY, l_run = 0.f;
   f32x4* xch_mine = lds_xch + w * 64 + lane;
   const f32x4* xch_grp = lds_xch + rg * SUB * 64 + lane;
+  if (tid < RG) lds_resc[tid] = -1;
+  int tile_no = 0;
 
   // One 32-token sub-tile of a resident stage.
   auto tile = [&](const uint8_t* kv, const float* sc, int sub, int32_t jt) {
@@ -406,10 +434,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p)
 #pragma unroll
       for (int k2 = 1; k2 < NKP; ++k2) sacc[t2] += xch_grp[(t2 + 2 * k2) * 64];
     }
-    // ---- online softmax (base 2), lane holds tokens tb*16 + 4g + i of row j
+    // ---- online softmax (base 2), lane holds tokens t2*16 + 4g + i of row j.
+    // The running maximum only moves when some score exceeds it by kTau; that
+    // is detected with a ballot and only then is the row maximum formed
+    // across the lanes of the row.
     const int tb0 = 32 * sub;
     float sv[8], tsc[8];
-    float mt = -INFINITY;
+    float mloc = -INFINITY;
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
@@ -422,14 +453,17 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p)
         }
         x = (jt + t < jlim) ? x : -INFINITY;
         sv[t2 * 4 + i] = x;
-        mt = fmaxf(mt, x);
+        mloc = fmaxf(mloc, x);
       }
     }
-    mt = wave_max_g(mt);
     float alpha = 1.f;
-    if (mt > m_run + kTau) {  // also true when m_run is -inf and the tile has a visible token
-      alpha = exp2f(m_run - mt);
-      m_run = mt;
+    const bool resc = __any(mloc > m_run + kTau);  // also true on the first visible tile
+    if (resc) {
+      const float mt = wave_max_g(mloc);
+      if (mt > m_run + kTau) {
+        alpha = exp2f(m_run - mt);
+        m_run = mt;
+      }
     }
     const float mref = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
@@ -442,15 +476,30 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p)
       pf[e] = (__bf16)pe;
     }
     l_run = l_run * alpha + psum;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) acc[d] *= alpha;
+    if (sw == 0) {  // one wave per row group publishes P^T (and the rescale factors)
+      lds_p[rg * 64 + lane] = pf;
+      if (resc) {
+        if (g == 0) lds_alpha[rg * 16 + j] = alpha;
+        if (lane == 0) lds_resc[rg] = tile_no;
+      }
     }
-    // ---- O^T += V^T . P^T for this wave's output columns
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P^T is in LDS
+    wg_barrier();
+    // ---- O^T += V^T . P^T for this wave's output blocks, every row group
+    bf16x8 pg[RG];
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+      pg[q] = lds_p[q * 64 + lane];
+      if (lds_resc[q] == tile_no) {
+        const float a = lds_alpha[q * 16 + j];
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) acc[d][q] *= a;
+      }
+    }
+    ++tile_no;
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
-      if (d % kSchedV == 0 && d > 0) __builtin_amdgcn_sched_barrier(0);
-      const int db = sw * NDB + d;
+      const int db = w * NDB + d;
       bf16x8 a;
       if (FP8) {
         i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(DCP_LDS(i32x2, kv + voff[sub][db & 3] + 64 * (db >> 2)));
@@ -462,7 +511,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p)
         i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         a = __builtin_bit_cast(bf16x8, v);
       }
-      acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, acc[d], 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < RG; ++q) acc[d][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pg[q], acc[d][q], 0, 0, 0);
     }
   };
 
@@ -488,24 +538,368 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p)
     const float* sc = lds_sc + (FP8 ? (s % kStages) * STOK : 0);
     const int32_t j0 = j_begin + s * STOK;
     tile(kv, sc, 0, j0);
-    if (NSUB == 2 && j0 + 32 < j_end) {
-      wg_barrier();  // every wave has read the exchanged slices
-      tile(kv, sc, 1, j0 + 32);
-    }
+    // The second e4m3 sub-tile reuses the exchange and P^T buffers: every wave
+    // read the slices before the P^T barrier and finished its PV before the
+    // next slice barrier, so no extra barrier is needed.
+    if (NSUB == 2 && j0 + 32 < j_end) tile(kv, sc, 1, j0 + 32);
   }
 
   // ---- finalise: o = O / l, lse = m + log2(l) (then base conversion)
   const float l_tot = wave_sum_g(l_run);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  float* orow_ptr = p.o_out + orow * kDv;
-#pragma unroll
-  for (int d = 0; d < NDB; ++d) {
-    const int col = (sw * NDB + d) * 16 + 4 * g;
-    *reinterpret_cast<f32x4*>(orow_ptr + col) = acc[d] * inv;
+  if (sw == 0) {
+    if (g == 0) {
+      lds_l[rg * 16 + j] = l_tot;
+      const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+      p.lse_out[orow] = p.out_base2 ? lse2 : lse2 * kLn2;
+    }
   }
-  if (sw == 0 && g == 0) {
-    float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
-    p.lse_out[orow] = p.out_base2 ? lse2 : lse2 * kLn2;
+  __syncthreads();
+  const int64_t orow0 = (((int64_t)rl * p.batch + b) * p.splits + split) * p.rows + rb * MB + j;
+#pragma unroll
+  for (int q = 0; q < RG; ++q) {
+    const float lq = lds_l[q * 16 + j];
+    const float inv = lq > 0.f ? 1.0f / lq : 0.f;
+    float* optr = p.o_out + (orow0 + q * 16) * kDv;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      const int col = (w * NDB + d) * 16 + 4 * g;
+      *reinterpret_cast<f32x4*>(optr + col) = acc[d][q] * inv;
+    }
+  }
+}
+
+// Producer/consumer variant for workgroups of 64 query rows (4 row blocks).
+// Waves 0-3 (one per SIMD) produce: wave q owns row block q, computes its full
+// S^T (both 16-token blocks, all 576 columns), the online softmax and P^T,
+// and publishes P^T (with the rescale factors when the running maximum
+// moved) in a double-buffered LDS area.  Waves 4-7 consume: wave 4+c owns
+// output columns [128c, 128c+128) of all 64 rows and multiplies V^T by the P^T
+// of the previous tile, so each transposed V fragment feeds four MFMAs.  One
+// workgroup barrier per tile hands P^T over and recycles the stage the
+// consumers finished; producer and consumer of a SIMD run different phases
+// and overlap.
+template <bool FP8, bool ALIGNED>
+__global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams p) {
+  constexpr int RGN = 4;                  // row blocks per workgroup
+  constexpr int MB = 16 * RGN;
+  constexpr int ROWB = FP8 ? kDqk : 2 * kDqk;
+  constexpr int CH = ROWB / 16;
+  constexpr int STOK = 32;                // tokens per stage (one tile)
+  constexpr int SBYTES = STOK * ROWB;     // 36864 (bf16) or 18432 (e4m3)
+  constexpr int NSTG = FP8 ? 8 : 4;       // ring stages
+  constexpr int NI_ALL = SBYTES / 1024;   // 1 KB direct-to-LDS loads per stage
+  constexpr int NI_MAX = (NI_ALL + kWaves - 1) / kWaves;
+  constexpr int NDBC = 8;                 // output blocks per consumer wave
+  constexpr int KU = FP8 ? 9 : 18;        // k units (k-steps, or e4m3 k-step pairs)
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv[NSTG * SBYTES];
+  __shared__ __attribute__((aligned(16))) float lds_sc[FP8 ? NSTG * STOK : 4];
+  __shared__ int32_t lds_pt[kMaxTab];
+  __shared__ __attribute__((aligned(16))) bf16x8 lds_p[2][RGN * 64];
+  __shared__ float lds_alpha[2][RGN * 16];
+  __shared__ int lds_resc[2][RGN];
+  __shared__ float lds_l[RGN * 16];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, j = lane & 15;
+  const bool producer = w < RGN;
+  const int rbq = w & 3;                  // producer: its row block
+  const int cq = w & 3;                   // consumer: its column group
+
+  const int64_t id = blockIdx.x;
+  const int xcd = (int)(id & 7);
+  const int64_t qq = id >> 3;
+  const int rb = (int)(qq % p.n_row_blocks);
+  const int64_t unit = (qq / p.n_row_blocks) * 8 + xcd;
+  if (unit >= p.units_total) return;
+  const int split = (int)(unit % p.splits);
+  const int64_t rbu = unit / p.splits;
+  const int b = (int)(rbu % p.batch);
+  const int rl = (int)(rbu / p.batch);
+  const int64_t r = (int64_t)p.rank_begin + rl;
+  const int64_t c = p.c, P = p.page;
+  const int row0 = rb * MB + rbq * 16;    // producer's first row
+
+  int32_t L = p.seq_len[b];
+  bool ok = true;
+  if (L < 0 || (int64_t)L > p.max_seq_len) {
+    if (tid == 0 && p.dev_status) atomicMax(p.dev_status, DCP_DEV_BAD_LENGTH);
+    ok = false;
+  } else if (((int64_t)L + P * c - 1) / (P * c) > p.bt_stride) {
+    if (tid == 0 && p.dev_status) atomicMax(p.dev_status, DCP_DEV_TABLE_OVERFLOW);
+    ok = false;
+  }
+  if (!ok) L = 0;
+  const int32_t ri = (int32_t)r, ci32 = (int32_t)c, Pi = (int32_t)P;
+  const int32_t n_r = L > ri ? (L - ri + ci32 - 1) / ci32 : 0;
+  auto visible = [&](int qi) -> int32_t {
+    int32_t lim = p.causal ? L - p.q_len + qi : L - 1;
+    if (lim < ri) return 0;
+    int32_t n = (lim - ri) / ci32 + 1;
+    return n < n_r ? n : n_r;
+  };
+  const int32_t split_tok = (int32_t)p.split_tokens;
+  const int32_t j_begin = split * split_tok;
+  const int32_t n_wg = visible((rb * MB + MB - 1) / p.heads);
+  const int32_t j_end = min(n_wg, j_begin + split_tok);
+  const int32_t jlim = min(visible(row0 / p.heads), j_begin + split_tok);
+  const int n_st = j_end > j_begin ? (j_end - j_begin + STOK - 1) / STOK : 0;
+
+  const uint8_t* pool = p.pools + (int64_t)rl * p.pool_bytes;
+  const float* spool = FP8 ? p.pool_scales + (int64_t)rl * p.cap : nullptr;
+  const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
+  const int32_t vp_first = j_begin / Pi;
+  const int32_t n_tab = n_st > 0 ? (j_end - 1) / Pi - vp_first + 1 : 0;
+  {
+    bool bad_page = false;
+    for (int t = tid; t < n_tab; t += kThreads) {
+      int32_t pg = bt[vp_first + t];
+      if ((unsigned)pg >= (unsigned)p.num_pages) {
+        bad_page = true;
+        pg = 0;
+      }
+      lds_pt[t] = pg;
+    }
+    if (bad_page && p.dev_status) atomicMax(p.dev_status, DCP_DEV_BAD_PAGE);
+  }
+  if (tid < 2 * RGN) lds_resc[tid / RGN][tid % RGN] = -1;
+
+  // One register array serves both roles, which are fixed per wave: a
+  // producer keeps its Q^T fragments (18 x 16 bytes) in R[0..17], a consumer
+  // its O^T accumulators (8 blocks x 4 row blocks) in R[0..31].
+  f32x4 R[NDBC * RGN];
+  if (producer) {
+    const uint16_t* qrow = p.q + ((int64_t)b * p.rows + row0 + j) * kDqk;
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) {
+      const int col = FP8 ? 64 * (kk >> 1) + 16 * g + 8 * (kk & 1) : 32 * kk + 8 * g;
+      R[kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + col));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NDBC * RGN; ++i) R[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto qf = [&](int kk) { return __builtin_bit_cast(bf16x8, R[kk]); };
+  wait_vmcnt<0>();  // Q and the page table have landed (see mla_decode_kernel)
+  __syncthreads();
+
+  // direct-to-LDS loads (same scheme as mla_decode_kernel)
+  const int ni = (w < NI_ALL % kWaves) ? NI_MAX : NI_MAX - 1;
+  int dma_row[NI_MAX];
+  uint32_t dma_off[NI_MAX];
+#pragma unroll
+  for (int t = 0; t < NI_MAX; ++t) {
+    const int ci = (w + kWaves * t) * 64 + lane;
+    const int row = min(ci / CH, STOK - 1);
+    dma_row[t] = row;
+    dma_off[t] = (uint32_t)(row * ROWB + ((ci % CH) ^ swz<FP8>(row)) * 16);
+  }
+  const int32_t jb_off = j_begin - vp_first * Pi;
+  auto slot_of = [&](int32_t jj) -> int64_t {
+    const int32_t pidx = jj / Pi;
+    return (int64_t)lds_pt[pidx - vp_first] * Pi + (jj - pidx * Pi);
+  };
+  auto issue = [&](int s) {
+    uint8_t* dst = lds_kv + (s % NSTG) * SBYTES;
+    float* dst_sc = lds_sc + (FP8 ? (s % NSTG) * STOK : 0);
+    const int32_t j0 = j_begin + s * STOK;
+    if (ALIGNED && j0 + STOK <= j_end) {
+      const int32_t rel = jb_off + s * STOK;
+      const int32_t pidx = rel / Pi;
+      const int32_t pg = __builtin_amdgcn_readfirstlane(lds_pt[pidx]);
+      const int64_t slot0 = (int64_t)pg * Pi + (rel - pidx * Pi);
+      const uint8_t* base = pool + slot0 * ROWB;
+#pragma unroll
+      for (int t = 0; t < NI_MAX; ++t)
+        if (t < ni) dma16(base, dma_off[t], dst + (w + kWaves * t) * 1024);
+      if (FP8 && lane < 4) dma4_abs(spool + slot0 + 4 * w + lane, dst_sc + 4 * w);
+    } else {
+#pragma unroll
+      for (int t = 0; t < NI_MAX; ++t)
+        if (t < ni) {
+          const int32_t jj = min(j0 + dma_row[t], j_end - 1);
+          dma16_abs(pool + slot_of(jj) * ROWB + (dma_off[t] - dma_row[t] * ROWB), dst + (w + kWaves * t) * 1024);
+        }
+      if (FP8) {
+        const int32_t jj = min(j0 + 4 * w + (lane & 3), j_end - 1);
+        const float* src = spool + slot_of(jj);
+        if (lane < 4) dma4_abs(src, dst_sc + 4 * w);
+      }
+    }
+  };
+
+  // producer K offsets (both token blocks) and consumer V^T offsets
+  int koff[2][2], voff[2][4];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int row = 16 * tb + j;
+    if (FP8) {
+      koff[tb][0] = row * ROWB + 16 * (g ^ swz<true>(row));
+      koff[tb][1] = koff[tb][0];
+    } else {
+#pragma unroll
+      for (int par = 0; par < 2; ++par) koff[tb][par] = row * ROWB + 16 * ((4 * par + g) ^ swz<false>(row));
+    }
+  }
+  if (FP8) {
+    const int s8 = (lane & 15) >> 1;
+    const int vrow = s8 < 4 ? 4 * (lane >> 4) + s8 : 16 + 4 * (lane >> 4) + (s8 - 4);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) voff[0][m] = vrow * ROWB + 16 * (m ^ swz<true>(vrow)) + 8 * (lane & 1);
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int vrow = 16 * h + 4 * (lane >> 4) + ((lane >> 2) & 3);
+      const int y = ((lane & 3) >> 1) ^ swz<false>(vrow);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) voff[h][m] = vrow * ROWB + 16 * ((2 * m) ^ y) + 8 * (lane & 1);
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;   // producer softmax state of row row0 + j
+
+  auto produce = [&](int t) {
+    const uint8_t* kv = lds_kv + (t % NSTG) * SBYTES;
+    const float* sc = lds_sc + (FP8 ? (t % NSTG) * STOK : 0);
+    const int32_t jt = j_begin + t * STOK;
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      if (u % kSchedK == 0 && u > 0) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        if (FP8) {
+          const i32x4 raw = *reinterpret_cast<const i32x4*>(kv + koff[tb][0] + 64 * u);
+          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{raw[0], raw[1]}), qf(2 * u), sacc[tb], 0, 0, 0);
+          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{raw[2], raw[3]}), qf(2 * u + 1), sacc[tb], 0, 0, 0);
+        } else {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kv + koff[tb][u & 1] + 128 * (u >> 1));
+          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf(u), sacc[tb], 0, 0, 0);
+        }
+      }
+    }
+    float sv[8], tsc[8];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tk = t2 * 16 + 4 * g + i;
+        float x = sacc[t2][i] * p.scale_log2;
+        if (FP8) {
+          tsc[t2 * 4 + i] = sc[tk];
+          x *= tsc[t2 * 4 + i];
+        }
+        x = (jt + tk < jlim) ? x : -INFINITY;
+        sv[t2 * 4 + i] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    }
+    float alpha = 1.f;
+    const bool resc = __any(mloc > m_run + kTau);
+    if (resc) {
+      const float mt = wave_max_g(mloc);
+      if (mt > m_run + kTau) {
+        alpha = exp2f(m_run - mt);
+        m_run = mt;
+      }
+    }
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
+    bf16x8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float pe = exp2f(sv[e] - mref);
+      psum += pe;
+      if (FP8) pe *= tsc[e];
+      pf[e] = (__bf16)pe;
+    }
+    l_run = l_run * alpha + psum;
+    lds_p[t & 1][rbq * 64 + lane] = pf;
+    if (resc) {
+      if (g == 0) lds_alpha[t & 1][rbq * 16 + j] = alpha;
+      if (lane == 0) lds_resc[t & 1][rbq] = t;
+    }
+  };
+
+  auto consume = [&](int t) {
+    const uint8_t* kv = lds_kv + (t % NSTG) * SBYTES;
+    bf16x8 pg[RGN];
+#pragma unroll
+    for (int q = 0; q < RGN; ++q) {
+      pg[q] = lds_p[t & 1][q * 64 + lane];
+      if (lds_resc[t & 1][q] == t) {
+        const float a = lds_alpha[t & 1][q * 16 + j];
+#pragma unroll
+        for (int d = 0; d < NDBC; ++d) R[d * RGN + q] *= a;
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < NDBC; ++d) {
+      const int db = cq * NDBC + d;
+      bf16x8 a;
+      if (FP8) {
+        i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(DCP_LDS(i32x2, kv + voff[0][db & 3] + 64 * (db >> 2)));
+        a = cvt_fp8x8(raw);
+      } else {
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DCP_LDS(i16x4, kv + voff[0][db & 3] + 128 * (db >> 2)));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DCP_LDS(i16x4, kv + voff[1][db & 3] + 128 * (db >> 2)));
+        typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+        i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        a = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int q = 0; q < RGN; ++q) R[d * RGN + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pg[q], R[d * RGN + q], 0, 0, 0);
+    }
+  };
+
+  // stages 0 .. NSTG-2 in flight; stage 0 resident before the first tile
+  for (int s = 0; s < NSTG - 1 && s < n_st; ++s) issue(s);
+  if (n_st > 0) {
+    // outstanding after stage 0: stages 1 .. min(NSTG-2, n_st-1)
+    wait_vmcnt_ahead<NI_MAX, NI_ALL % kWaves, FP8, NSTG - 2>(w, min(NSTG - 2, n_st - 1));
+  }
+  wg_barrier();
+  for (int i = 0; i <= n_st; ++i) {
+    if (producer) {
+      if (i < n_st) produce(i);
+    } else if (i >= 1) {
+      consume(i - 1);
+    }
+    if (i == n_st) break;
+    // stage i+1 must be resident for the next producer tile
+    if (i + 1 < n_st) wait_vmcnt_ahead<NI_MAX, NI_ALL % kWaves, FP8, NSTG - 2>(w, min(NSTG - 3, n_st - 2 - i));
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P^T and the rescale factors are in LDS
+    wg_barrier();
+    // the consumers are done with stage i-1: refill its slot
+    if (i + NSTG - 1 < n_st) issue(i + NSTG - 1);
+  }
+
+  // ---- finalise
+  if (producer) {
+    const float l_tot = wave_sum_g(l_run);
+    if (g == 0) {
+      lds_l[rbq * 16 + j] = l_tot;
+      const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+      const int64_t orow = (((int64_t)rl * p.batch + b) * p.splits + split) * p.rows + row0 + j;
+      p.lse_out[orow] = p.out_base2 ? lse2 : lse2 * kLn2;
+    }
+  }
+  __syncthreads();
+  if (!producer) {
+    const int64_t orow0 = (((int64_t)rl * p.batch + b) * p.splits + split) * p.rows + rb * MB + j;
+#pragma unroll
+    for (int q = 0; q < RGN; ++q) {
+      const float lq = lds_l[q * 16 + j];
+      const float inv = lq > 0.f ? 1.0f / lq : 0.f;
+      float* optr = p.o_out + (orow0 + q * 16) * kDv;
+#pragma unroll
+      for (int d = 0; d < NDBC; ++d) {
+        const int col = (cq * NDBC + d) * 16 + 4 * g;
+        *reinterpret_cast<f32x4*>(optr + col) = R[d * RGN + q] * inv;
+      }
+    }
   }
 }
 
@@ -530,6 +924,12 @@ split_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ w
 template <int RG, bool FP8, bool ALIGNED>
 hipError_t launch_variant(const DecodeParams& prm, int64_t grid, hipStream_t stream) {
   hipLaunchKernelGGL((mla_decode_kernel<RG, FP8, ALIGNED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, prm);
+  return hipGetLastError();
+}
+
+template <bool FP8, bool ALIGNED>
+hipError_t launch_pc(const DecodeParams& prm, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((mla_decode_pc_kernel<FP8, ALIGNED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, prm);
   return hipGetLastError();
 }
 
@@ -559,7 +959,7 @@ DecodePlan plan_decode(int32_t c, int32_t page, bool fp8, int32_t rank_count, in
   const int rg = pl.rows % 64 == 0 ? 4 : (pl.rows % 32 == 0 ? 2 : 1);
   pl.row_block = 16 * rg;
   pl.n_row_blocks = pl.rows / pl.row_block;
-  pl.stage_tokens = fp8 ? 64 : 32;
+  pl.stage_tokens = (fp8 && rg < 4) ? 64 : 32;  // the 64-row kernel streams 32-token stages
   const int64_t n_r_max = (max_seq_len + c - 1) / c;
   const int64_t stages_max = (n_r_max + pl.stage_tokens - 1) / pl.stage_tokens;
   const int64_t units = (int64_t)rank_count * batch * pl.n_row_blocks;
@@ -629,12 +1029,15 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   const int64_t grid = (prm.units_total + 7) / 8 * 8 * pl.n_row_blocks;
   hipError_t e;
   const int rg = pl.row_block / 16;
-  if (a.fp8) {
-    e = rg == 4 ? launch_rg<4, true>(prm, aligned, grid, stream)
-                : rg == 2 ? launch_rg<2, true>(prm, aligned, grid, stream) : launch_rg<1, true>(prm, aligned, grid, stream);
+  if (rg == 4) {
+    if (a.fp8)
+      e = aligned ? launch_pc<true, true>(prm, grid, stream) : launch_pc<true, false>(prm, grid, stream);
+    else
+      e = aligned ? launch_pc<false, true>(prm, grid, stream) : launch_pc<false, false>(prm, grid, stream);
+  } else if (a.fp8) {
+    e = rg == 2 ? launch_rg<2, true>(prm, aligned, grid, stream) : launch_rg<1, true>(prm, aligned, grid, stream);
   } else {
-    e = rg == 4 ? launch_rg<4, false>(prm, aligned, grid, stream)
-                : rg == 2 ? launch_rg<2, false>(prm, aligned, grid, stream) : launch_rg<1, false>(prm, aligned, grid, stream);
+    e = rg == 2 ? launch_rg<2, false>(prm, aligned, grid, stream) : launch_rg<1, false>(prm, aligned, grid, stream);
   }
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t n_rows_total = (int64_t)a.rank_count * a.batch * pl.rows;
