@@ -106,8 +106,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // writes.  m0 carries the LDS address; nothing else in these kernels uses m0
 // (a host-side build check verifies this in the generated code).
 __device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, const void* lds) {
+  // gbase is wave-uniform; readfirstlane pins it (and the LDS address) to SGPRs
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(gbase)
+  // (readfirstlane returns a signed int: widen through uint32_t, never sign-extend)
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)gbase);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uintptr_t)gbase >> 32));
+  const uint64_t gb = lo | (hi << 32);
+  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(gb)
                    : "memory");
 }
 __device__ __forceinline__ void dma16_abs(const uint8_t* gaddr, const void* lds) {

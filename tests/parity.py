@@ -28,14 +28,15 @@ def log(msg):
 class Case:
     """One workload's inputs on host and device, and its emulated group."""
 
-    def __init__(self, w: Workload, lens=None, needles=None, seed_free_stack=True, sentinel=None):
+    def __init__(self, w: Workload, lens=None, needles=None, seed_free_stack=True, sentinel=None,
+                 num_pages=None):
         from kv_sharded_mla_amd import KV_BF16, KV_FP8_E4M3
         from kv_sharded_mla_amd.group import DcpGroup
         self.w = w
         self.lens = gen.lengths(w) if lens is None else np.asarray(lens, dtype=np.int64)
         self.q_bits = gen.q_bits(w)
         self.needles = needles
-        self.num_pages = gen.pool_pages(w, self.lens)
+        self.num_pages = gen.pool_pages(w, self.lens) if num_pages is None else int(num_pages)
         vp = w.P * w.c
         self.bt_stride = max(1, max((int(L) + vp - 1) // vp for L in self.lens))
         fs = gen.free_stack(w, self.num_pages) if seed_free_stack else None

@@ -71,3 +71,19 @@ def test_repeat_runs_bitwise_stable():
     b = case.run()
     for x, y in zip(a, b):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+@pytest.mark.parametrize("kv,H", [("bf16", 16), ("bf16", 64), ("fp8", 64)])
+def test_decode_pages_beyond_4gib(kv, H):
+    # Regression: the 64-bit page base of the direct-to-LDS loads once picked up a
+    # sign-extended low word.  Four owner pools of about 1.25 GiB each, with an identity
+    # free stack handing out the highest page ids first, put the pages in use about
+    # 1.25 GiB apart across 5 GiB: whatever the allocation base, some of them have bit
+    # 31 of the low address word set.
+    row = 1152 if kv == "bf16" else 576
+    pages = (5 << 30) // (64 * row * 4) + 1
+    w = W(index=71, H=H, c=4, P=64, fixed_len=3000, B=2, kv_dtype=kv)
+    case = Case(w, seed_free_stack=False, num_pages=pages)
+    bt = case.group.block_table.cpu().numpy()
+    assert bt[bt >= 0].min() * 64 * row > (1 << 30)
+    check_case(case)
