@@ -84,7 +84,11 @@ struct DecodeParams {
 #endif
 template <bool FP8>
 __device__ __forceinline__ int swz(int r) {
-  if (FP8) return ((r >> 1) & 3) ^ ((r >> 3) & 3);
+  // e4m3 rows (576 B) start 16 banks apart, so rows r and r+4 share a 16-bank
+  // window; bits 2 and 3^4 of the row pick the chunk position inside it, which
+  // separates the 16 rows of a K read (rows 16t..16t+15) and of a transposed V
+  // read (rows 4G+s and 16+4G+s) alike
+  if (FP8) return ((r >> 2) & 1) | ((((r >> 3) ^ (r >> 4)) & 1) << 1);
 #if DCP_LDS_SWIZZLE == 0
   return 2 * (((r >> 1) ^ r) & 3) + ((r >> 2) & 1);  // no conflicts with 32 banks of 4 bytes
 #else
@@ -176,6 +180,52 @@ __device__ __forceinline__ float wave_sum_g(float v) {
   return v;
 }
 
+// Workgroup -> (row block, work unit).  Workgroup ids congruent mod 8 run on
+// the same XCD; the row blocks of one unit get ids congruent mod 8 so their KV
+// reads share that XCD's L2.  Each block of 8 consecutive units is rotated
+// across the XCDs by a mix of the block index, so that the splits and ranks
+// of one request spread over all XCDs even when a ragged batch concentrates
+// the work in a few units.
+struct WgUnit {
+  int rb;
+  int64_t unit;
+};
+__device__ __forceinline__ WgUnit wg_unit(int64_t id, int n_row_blocks) {
+  const int xcd = (int)(id & 7);
+  const int64_t qq = id >> 3;
+  const int64_t blk = qq / n_row_blocks;
+  const int rot = (int)((blk + (blk >> 3) + (blk >> 6)) & 7);
+  return WgUnit{(int)(qq % n_row_blocks), blk * 8 + ((xcd + rot) & 7)};
+}
+
+// Global KV length of request b, or 0 when it is negative, above max_seq_len
+// or needs more pages than a block-table row holds (reported when `report`).
+__device__ __forceinline__ int32_t request_len(const DecodeParams& p, int b, bool report) {
+  const int32_t L = p.seq_len[b];
+  const int64_t vp = (int64_t)p.page * p.c;
+  if (L < 0 || (int64_t)L > p.max_seq_len) {
+    if (report && p.dev_status) atomicMax(p.dev_status, DCP_DEV_BAD_LENGTH);
+    return 0;
+  }
+  if (((int64_t)L + vp - 1) / vp > p.bt_stride) {
+    if (report && p.dev_status) atomicMax(p.dev_status, DCP_DEV_TABLE_OVERFLOW);
+    return 0;
+  }
+  return L;
+}
+
+// Rank-local tokens of rank r that query index qi sees: rank r owns positions
+// j*c + r (j < n_r); a causal query qi of a q_len-token verification step sits
+// at global position L - q_len + qi and sees positions up to it.
+__device__ __forceinline__ int32_t visible_tokens(int32_t L, int32_t r, int32_t c, int32_t q_len, int32_t qi,
+                                                  int32_t causal) {
+  const int32_t n_r = L > r ? (L - r + c - 1) / c : 0;
+  const int32_t lim = causal ? L - q_len + qi : L - 1;
+  if (lim < r) return 0;
+  const int32_t n = (lim - r) / c + 1;
+  return n < n_r ? n : n_r;
+}
+
 template <int RG, bool FP8, bool ALIGNED>
 __global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p) {
   constexpr int SUB = kWaves / RG;        // waves per row group
@@ -217,11 +267,9 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p)
 
   // XCD-aware unit mapping: the row blocks of one (rank, request, split) sit on
   // the same XCD (ids congruent mod 8) so their KV reads share that L2.
-  const int64_t id = blockIdx.x;
-  const int xcd = (int)(id & 7);
-  const int64_t qq = id >> 3;
-  const int rb = (int)(qq % p.n_row_blocks);
-  const int64_t unit = (qq / p.n_row_blocks) * 8 + xcd;
+  const WgUnit wu = wg_unit(blockIdx.x, p.n_row_blocks);
+  const int rb = wu.rb;
+  const int64_t unit = wu.unit;
   if (unit >= p.units_total) return;
   const int split = (int)(unit % p.splits);
   const int64_t rbu = unit / p.splits;
@@ -233,32 +281,21 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p)
   const int row0 = rb * MB + rg * 16;     // first query row of this wave's row group
   const int64_t orow = (((int64_t)rl * p.batch + b) * p.splits + split) * p.rows + row0 + j;
 
-  int32_t L = p.seq_len[b];
-  bool ok = true;
-  if (L < 0 || (int64_t)L > p.max_seq_len) {
-    if (tid == 0 && p.dev_status) atomicMax(p.dev_status, DCP_DEV_BAD_LENGTH);
-    ok = false;
-  } else if (((int64_t)L + P * c - 1) / (P * c) > p.bt_stride) {
-    if (tid == 0 && p.dev_status) atomicMax(p.dev_status, DCP_DEV_TABLE_OVERFLOW);
-    ok = false;
-  }
-  if (!ok) L = 0;
+  const int32_t L = request_len(p, b, tid == 0);
 
   // all rank-local token indices fit in int32 (seq_len is int32)
-  const int32_t ri = (int32_t)r, ci32 = (int32_t)c, Pi = (int32_t)P;
-  const int32_t n_r = L > ri ? (L - ri + ci32 - 1) / ci32 : 0;
-  auto visible = [&](int qi) -> int32_t {  // rank-local tokens visible to query index qi
-    int32_t lim = p.causal ? L - p.q_len + qi : L - 1;
-    if (lim < ri) return 0;
-    int32_t n = (lim - ri) / ci32 + 1;
-    return n < n_r ? n : n_r;
-  };
+  const int32_t ri = (int32_t)r, Pi = (int32_t)P;
+  auto visible = [&](int qi) -> int32_t { return visible_tokens(L, ri, p.c, p.q_len, qi, p.causal); };
   const int32_t split_tok = (int32_t)p.split_tokens;
   const int32_t j_begin = split * split_tok;
   const int32_t n_wg = visible((rb * MB + MB - 1) / p.heads);
   const int32_t j_end = min(n_wg, j_begin + split_tok);
   const int32_t jlim = min(visible(row0 / p.heads), j_begin + split_tok);
   const int n_st = j_end > j_begin ? (j_end - j_begin + STOK - 1) / STOK : 0;
+  // a split past the end of every row of the block writes nothing (the split
+  // combine reads only the splits that hold visible tokens of a row); split 0
+  // always writes, so that an empty shard still yields lse = -inf and o = 0
+  if (n_st == 0 && split > 0) return;
 
   const uint8_t* pool = p.pools + (int64_t)rl * p.pool_bytes;
   const float* spool = FP8 ? p.pool_scales + (int64_t)rl * p.cap : nullptr;
@@ -582,7 +619,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p)
 // of the previous tile, so each transposed V fragment feeds four MFMAs.  One
 // workgroup barrier per tile hands P^T over and recycles the stage the
 // consumers finished; producer and consumer of a SIMD run different phases
-// and overlap.
+// and overlap.  Producers run at a raised wave priority, so their MFMAs go
+// first and the consumer's MFMAs fill the time of the producer's softmax;
+// the consumers also issue every direct-to-LDS load, which keeps the
+// producers' path from one barrier to the next free of load issue and waits.
 template <bool FP8, bool ALIGNED>
 __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams p) {
   constexpr int RGN = 4;                  // row blocks per workgroup
@@ -593,7 +633,9 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   constexpr int SBYTES = STOK * ROWB;     // 36864 (bf16) or 18432 (e4m3)
   constexpr int NSTG = FP8 ? 8 : 4;       // ring stages
   constexpr int NI_ALL = SBYTES / 1024;   // 1 KB direct-to-LDS loads per stage
-  constexpr int NI_MAX = (NI_ALL + kWaves - 1) / kWaves;
+  constexpr int NLW = 4;                  // loading (consumer) waves
+  constexpr int NI_MAX = (NI_ALL + NLW - 1) / NLW;            // loads of the busiest loading wave
+  constexpr int NBIG = NI_ALL % NLW == 0 ? NLW : NI_ALL % NLW;  // loading waves that issue NI_MAX
   constexpr int NDBC = 8;                 // output blocks per consumer wave
   constexpr int KU = FP8 ? 9 : 18;        // k units (k-steps, or e4m3 k-step pairs)
 
@@ -602,7 +644,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   __shared__ int32_t lds_pt[kMaxTab];
   __shared__ __attribute__((aligned(16))) bf16x8 lds_p[2][RGN * 64];
   __shared__ float lds_alpha[2][RGN * 16];
-  __shared__ int lds_resc[2][RGN];
+  __shared__ __attribute__((aligned(16))) int lds_resc[2][RGN];
   __shared__ float lds_l[RGN * 16];
 
   const int tid = threadIdx.x;
@@ -612,11 +654,9 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   const int rbq = w & 3;                  // producer: its row block
   const int cq = w & 3;                   // consumer: its column group
 
-  const int64_t id = blockIdx.x;
-  const int xcd = (int)(id & 7);
-  const int64_t qq = id >> 3;
-  const int rb = (int)(qq % p.n_row_blocks);
-  const int64_t unit = (qq / p.n_row_blocks) * 8 + xcd;
+  const WgUnit wu = wg_unit(blockIdx.x, p.n_row_blocks);
+  const int rb = wu.rb;
+  const int64_t unit = wu.unit;
   if (unit >= p.units_total) return;
   const int split = (int)(unit % p.splits);
   const int64_t rbu = unit / p.splits;
@@ -626,30 +666,20 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   const int64_t c = p.c, P = p.page;
   const int row0 = rb * MB + rbq * 16;    // producer's first row
 
-  int32_t L = p.seq_len[b];
-  bool ok = true;
-  if (L < 0 || (int64_t)L > p.max_seq_len) {
-    if (tid == 0 && p.dev_status) atomicMax(p.dev_status, DCP_DEV_BAD_LENGTH);
-    ok = false;
-  } else if (((int64_t)L + P * c - 1) / (P * c) > p.bt_stride) {
-    if (tid == 0 && p.dev_status) atomicMax(p.dev_status, DCP_DEV_TABLE_OVERFLOW);
-    ok = false;
-  }
-  if (!ok) L = 0;
-  const int32_t ri = (int32_t)r, ci32 = (int32_t)c, Pi = (int32_t)P;
-  const int32_t n_r = L > ri ? (L - ri + ci32 - 1) / ci32 : 0;
-  auto visible = [&](int qi) -> int32_t {
-    int32_t lim = p.causal ? L - p.q_len + qi : L - 1;
-    if (lim < ri) return 0;
-    int32_t n = (lim - ri) / ci32 + 1;
-    return n < n_r ? n : n_r;
-  };
+  const int32_t L = request_len(p, b, tid == 0);
+  // all rank-local token indices fit in int32 (seq_len is int32)
+  const int32_t ri = (int32_t)r, Pi = (int32_t)P;
+  auto visible = [&](int qi) -> int32_t { return visible_tokens(L, ri, p.c, p.q_len, qi, p.causal); };
   const int32_t split_tok = (int32_t)p.split_tokens;
   const int32_t j_begin = split * split_tok;
   const int32_t n_wg = visible((rb * MB + MB - 1) / p.heads);
   const int32_t j_end = min(n_wg, j_begin + split_tok);
   const int32_t jlim = min(visible(row0 / p.heads), j_begin + split_tok);
   const int n_st = j_end > j_begin ? (j_end - j_begin + STOK - 1) / STOK : 0;
+  // a split past the end of every row of the block writes nothing (the split
+  // combine reads only the splits that hold visible tokens of a row); split 0
+  // always writes, so that an empty shard still yields lse = -inf and o = 0
+  if (n_st == 0 && split > 0) return;
 
   const uint8_t* pool = p.pools + (int64_t)rl * p.pool_bytes;
   const float* spool = FP8 ? p.pool_scales + (int64_t)rl * p.cap : nullptr;
@@ -689,47 +719,60 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   wait_vmcnt<0>();  // Q and the page table have landed (see mla_decode_kernel)
   __syncthreads();
 
-  // direct-to-LDS loads (same scheme as mla_decode_kernel)
-  const int ni = (w < NI_ALL % kWaves) ? NI_MAX : NI_MAX - 1;
+  // direct-to-LDS loads, issued by the consumer waves: loading wave lw issues
+  // loads lw, lw + 4, ... of a stage; load i fills LDS bytes [1024 i, 1024 i +
+  // 1024), lane k the 16 bytes at 1024 i + 16 k, which hold chunk
+  // (pos ^ swz(row)) of stage row `row` (pos = position inside the row)
+  const int lw = w & 3;
+  const int ni = producer ? 0 : (lw < NBIG ? NI_MAX : NI_MAX - 1);
   int dma_row[NI_MAX];
   uint32_t dma_off[NI_MAX];
 #pragma unroll
   for (int t = 0; t < NI_MAX; ++t) {
-    const int ci = (w + kWaves * t) * 64 + lane;
+    const int ci = (lw + NLW * t) * 64 + lane;
     const int row = min(ci / CH, STOK - 1);
     dma_row[t] = row;
     dma_off[t] = (uint32_t)(row * ROWB + ((ci % CH) ^ swz<FP8>(row)) * 16);
   }
-  const int32_t jb_off = j_begin - vp_first * Pi;
   auto slot_of = [&](int32_t jj) -> int64_t {
     const int32_t pidx = jj / Pi;
     return (int64_t)lds_pt[pidx - vp_first] * Pi + (jj - pidx * Pi);
   };
-  auto issue = [&](int s) {
+  // next stage to issue: entry iss_pidx of the page table, token iss_rem of
+  // that page (tracked only when stages never straddle pages)
+  int32_t iss_pidx = 0, iss_rem = j_begin - vp_first * Pi;
+  // issue stage s; pg is the page id of the stage (whole-stage fast path)
+  auto issue = [&](int s, int32_t pg) {
     uint8_t* dst = lds_kv + (s % NSTG) * SBYTES;
     float* dst_sc = lds_sc + (FP8 ? (s % NSTG) * STOK : 0);
     const int32_t j0 = j_begin + s * STOK;
     if (ALIGNED && j0 + STOK <= j_end) {
-      const int32_t rel = jb_off + s * STOK;
-      const int32_t pidx = rel / Pi;
-      const int32_t pg = __builtin_amdgcn_readfirstlane(lds_pt[pidx]);
-      const int64_t slot0 = (int64_t)pg * Pi + (rel - pidx * Pi);
+      const int64_t slot0 = (int64_t)pg * Pi + iss_rem;
       const uint8_t* base = pool + slot0 * ROWB;
 #pragma unroll
       for (int t = 0; t < NI_MAX; ++t)
-        if (t < ni) dma16(base, dma_off[t], dst + (w + kWaves * t) * 1024);
-      if (FP8 && lane < 4) dma4_abs(spool + slot0 + 4 * w + lane, dst_sc + 4 * w);
+        if (t < ni) dma16(base, dma_off[t], dst + (lw + NLW * t) * 1024);
+      if (FP8 && lane < 8) dma4_abs(spool + slot0 + 8 * lw + lane, dst_sc + 8 * lw);
     } else {
+      // last stage of a split (rows past j_end repeat the last valid row) or
+      // pages that a stage can straddle
 #pragma unroll
       for (int t = 0; t < NI_MAX; ++t)
         if (t < ni) {
           const int32_t jj = min(j0 + dma_row[t], j_end - 1);
-          dma16_abs(pool + slot_of(jj) * ROWB + (dma_off[t] - dma_row[t] * ROWB), dst + (w + kWaves * t) * 1024);
+          dma16_abs(pool + slot_of(jj) * ROWB + (dma_off[t] - dma_row[t] * ROWB), dst + (lw + NLW * t) * 1024);
         }
       if (FP8) {
-        const int32_t jj = min(j0 + 4 * w + (lane & 3), j_end - 1);
+        const int32_t jj = min(j0 + 8 * lw + (lane & 7), j_end - 1);
         const float* src = spool + slot_of(jj);
-        if (lane < 4) dma4_abs(src, dst_sc + 4 * w);
+        if (lane < 8) dma4_abs(src, dst_sc + 8 * lw);
+      }
+    }
+    if (ALIGNED) {
+      iss_rem += STOK;
+      if (iss_rem >= Pi) {
+        iss_rem -= Pi;
+        ++iss_pidx;
       }
     }
   };
@@ -769,23 +812,53 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     const float* sc = lds_sc + (FP8 ? (t % NSTG) * STOK : 0);
     const int32_t jt = j_begin + t * STOK;
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // K fragments f = 2u + tb (k unit u, token block tb), kept PD loads ahead
+    // of the MFMA that uses them; the schedule below pins that interleave.
+    if (FP8) {
+      constexpr int NF = 2 * KU, PD = 6;
+      i32x4 kf[NF];
+      auto kload = [&](int f) { return *reinterpret_cast<const i32x4*>(kv + koff[f & 1][0] + 64 * (f >> 1)); };
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      if (u % kSchedK == 0 && u > 0) __builtin_amdgcn_sched_barrier(0);
+      for (int f = 0; f < PD; ++f) kf[f] = kload(f);
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        if (FP8) {
-          const i32x4 raw = *reinterpret_cast<const i32x4*>(kv + koff[tb][0] + 64 * u);
-          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{raw[0], raw[1]}), qf(2 * u), sacc[tb], 0, 0, 0);
-          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{raw[2], raw[3]}), qf(2 * u + 1), sacc[tb], 0, 0, 0);
-        } else {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kv + koff[tb][u & 1] + 128 * (u >> 1));
-          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf(u), sacc[tb], 0, 0, 0);
-        }
+      for (int f = 0; f < NF; ++f) {
+        if (f + PD < NF) kf[f + PD] = kload(f + PD);
+        const int u = f >> 1, tb = f & 1;
+        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{kf[f][0], kf[f][1]}), qf(2 * u), sacc[tb], 0, 0, 0);
+        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{kf[f][2], kf[f][3]}), qf(2 * u + 1), sacc[tb], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
+#pragma unroll
+      for (int f = 0; f < NF - PD; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * PD, 0);
+    } else {
+      constexpr int NF = 2 * KU, PD = 8;
+      bf16x8 kf[NF];
+      auto kload = [&](int f) {
+        const int u = f >> 1;
+        return *reinterpret_cast<const bf16x8*>(kv + koff[f & 1][u & 1] + 128 * (u >> 1));
+      };
+#pragma unroll
+      for (int f = 0; f < PD; ++f) kf[f] = kload(f);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if (f + PD < NF) kf[f + PD] = kload(f + PD);
+        sacc[f & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f], qf(f >> 1), sacc[f & 1], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
+#pragma unroll
+      for (int f = 0; f < NF - PD; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, PD, 0);
     }
     float sv[8], tsc[8];
     float mloc = -INFINITY;
+    const bool whole = jt + STOK <= jlim;  // every token of the tile visible to this row block
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
@@ -796,7 +869,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
           tsc[t2 * 4 + i] = sc[tk];
           x *= tsc[t2 * 4 + i];
         }
-        x = (jt + tk < jlim) ? x : -INFINITY;
+        if (!whole) x = (jt + tk < jlim) ? x : -INFINITY;
         sv[t2 * 4 + i] = x;
         mloc = fmaxf(mloc, x);
       }
@@ -830,55 +903,68 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
 
   auto consume = [&](int t) {
     const uint8_t* kv = lds_kv + (t % NSTG) * SBYTES;
+    // every LDS read of the tile is issued first: the rescale flags, P^T of
+    // the four row blocks and the eight V^T fragments; the MFMAs then wait
+    // for them in issue order
+    const i32x4 resc = *reinterpret_cast<const i32x4*>(&lds_resc[t & 1][0]);
     bf16x8 pg[RGN];
 #pragma unroll
-    for (int q = 0; q < RGN; ++q) {
-      pg[q] = lds_p[t & 1][q * 64 + lane];
-      if (lds_resc[t & 1][q] == t) {
-        const float a = lds_alpha[t & 1][q * 16 + j];
-#pragma unroll
-        for (int d = 0; d < NDBC; ++d) R[d * RGN + q] *= a;
-      }
-    }
+    for (int q = 0; q < RGN; ++q) pg[q] = lds_p[t & 1][q * 64 + lane];
+    bf16x8 vf[NDBC];
 #pragma unroll
     for (int d = 0; d < NDBC; ++d) {
       const int db = cq * NDBC + d;
-      bf16x8 a;
       if (FP8) {
         i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(DCP_LDS(i32x2, kv + voff[0][db & 3] + 64 * (db >> 2)));
-        a = cvt_fp8x8(raw);
+        vf[d] = cvt_fp8x8(raw);
       } else {
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DCP_LDS(i16x4, kv + voff[0][db & 3] + 128 * (db >> 2)));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DCP_LDS(i16x4, kv + voff[1][db & 3] + 128 * (db >> 2)));
         typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
         i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        a = __builtin_bit_cast(bf16x8, v);
+        vf[d] = __builtin_bit_cast(bf16x8, v);
       }
-#pragma unroll
-      for (int q = 0; q < RGN; ++q) R[d * RGN + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pg[q], R[d * RGN + q], 0, 0, 0);
     }
+    if (resc[0] == t || resc[1] == t || resc[2] == t || resc[3] == t) {
+#pragma unroll
+      for (int q = 0; q < RGN; ++q)
+        if (resc[q] == t) {
+          const float a = lds_alpha[t & 1][q * 16 + j];
+#pragma unroll
+          for (int d = 0; d < NDBC; ++d) R[d * RGN + q] *= a;
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < NDBC; ++d)
+#pragma unroll
+      for (int q = 0; q < RGN; ++q)
+        R[d * RGN + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], pg[q], R[d * RGN + q], 0, 0, 0);
   };
 
   // stages 0 .. NSTG-2 in flight; stage 0 resident before the first tile
-  for (int s = 0; s < NSTG - 1 && s < n_st; ++s) issue(s);
-  if (n_st > 0) {
-    // outstanding after stage 0: stages 1 .. min(NSTG-2, n_st-1)
-    wait_vmcnt_ahead<NI_MAX, NI_ALL % kWaves, FP8, NSTG - 2>(w, min(NSTG - 2, n_st - 1));
+  if (!producer) {
+    for (int s = 0; s < NSTG - 1 && s < n_st; ++s) issue(s, ALIGNED ? __builtin_amdgcn_readfirstlane(lds_pt[iss_pidx]) : 0);
+    if (n_st > 0) wait_vmcnt_ahead<NI_MAX, NBIG, FP8, NSTG - 2>(lw, min(NSTG - 2, n_st - 1));
   }
   wg_barrier();
+  if (producer) __builtin_amdgcn_s_setprio(2);
   for (int i = 0; i <= n_st; ++i) {
+    const bool refill = i + NSTG - 1 < n_st;
+    int32_t pg_next = 0;
     if (producer) {
       if (i < n_st) produce(i);
-    } else if (i >= 1) {
-      consume(i - 1);
+    } else {
+      // page id of the stage issued after this tile's barrier, read early
+      if (ALIGNED && refill) pg_next = lds_pt[iss_pidx];
+      if (i >= 1) consume(i - 1);
     }
     if (i == n_st) break;
     // stage i+1 must be resident for the next producer tile
-    if (i + 1 < n_st) wait_vmcnt_ahead<NI_MAX, NI_ALL % kWaves, FP8, NSTG - 2>(w, min(NSTG - 3, n_st - 2 - i));
+    if (!producer && i + 1 < n_st) wait_vmcnt_ahead<NI_MAX, NBIG, FP8, NSTG - 2>(lw, min(NSTG - 3, n_st - 2 - i));
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P^T and the rescale factors are in LDS
     wg_barrier();
     // the consumers are done with stage i-1: refill its slot
-    if (i + NSTG - 1 < n_st) issue(i + NSTG - 1);
+    if (!producer && refill) issue(i + NSTG - 1, __builtin_amdgcn_readfirstlane(pg_next));
   }
 
   // ---- finalise
@@ -909,19 +995,27 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
 }
 
 // Merge the KV splits of every (rank, request, row): ws [units][splits][rows] -> o_part, lse_part.
+// Only the splits that hold visible tokens of the row are read (at least
+// split 0, which the decode kernel always writes).
 __global__ void __launch_bounds__(256)
-split_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int32_t splits,
-                     int32_t rows, int64_t n_rows_total, int32_t out_base2, float* __restrict__ o_part,
+split_combine_kernel(DecodeParams p, const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
+                     int64_t n_rows_total, int32_t out_base2, float* __restrict__ o_part,
                      float* __restrict__ lse_part) {
   const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
   const int col4 = threadIdx.x & 127;
   if (row >= n_rows_total) return;
-  const int64_t unit = row / rows, rr = row % rows;
-  const float* o = ws_o + (unit * splits * rows + rr) * kDv;
-  const float* l = ws_lse + unit * splits * rows + rr;
+  const int64_t unit = row / p.rows;
+  const int rr = (int)(row % p.rows);
+  const int b = (int)(unit % p.batch);
+  const int32_t rank = (int32_t)(p.rank_begin + unit / p.batch);
+  const int32_t L = request_len(p, b, false);
+  const int32_t vis = visible_tokens(L, rank, p.c, p.q_len, rr / p.heads, p.causal);
+  const int32_t nv = (int32_t)min<int64_t>(p.splits, max<int64_t>(1, (vis + p.split_tokens - 1) / p.split_tokens));
+  const float* o = ws_o + (unit * p.splits * p.rows + rr) * kDv;
+  const float* l = ws_lse + unit * p.splits * p.rows + rr;
   f32x4 acc;
   float lse2;
-  merge_row4(o, (int64_t)rows * kDv, l, rows, splits, true, col4, acc, lse2);
+  merge_row4(o, (int64_t)p.rows * kDv, l, p.rows, nv, true, col4, acc, lse2);
   *reinterpret_cast<f32x4*>(o_part + row * kDv + 4 * col4) = acc;
   if (col4 == 0) lse_part[row] = out_base2 ? lse2 : lse2 * kLn2;
 }
@@ -1046,8 +1140,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   }
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t n_rows_total = (int64_t)a.rank_count * a.batch * pl.rows;
-  hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)((n_rows_total + 1) / 2)), dim3(256), 0, stream, ws_o,
-                     ws_lse, pl.splits, pl.rows, n_rows_total, a.base2 ? 1 : 0, a.o_part, a.lse_part);
+  hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)((n_rows_total + 1) / 2)), dim3(256), 0, stream, prm,
+                     ws_o, ws_lse, n_rows_total, a.base2 ? 1 : 0, a.o_part, a.lse_part);
   return hipGetLastError();
 }
 

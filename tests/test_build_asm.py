@@ -51,9 +51,10 @@ def test_decode_kernels_do_not_spill(asm):
 def test_no_compiler_vmcnt_waits_inside_decode_loop(asm):
     # every vmcnt wait of the decode kernels is one of the explicit ones: 0 (page table and
     # Q before the loop, ring tail) or a whole number of stages of one wave's loads (3 to 6
-    # loads per stage).  A wait the compiler placed for Q inside the loop would show up as
-    # a count such as 17, 16, ... 1.
-    allowed = {0} | {k * n for n in (3, 4, 5, 6) for k in range(1, 7)}
+    # loads per stage, or 9 for the 64-row bf16 kernel whose four consumer waves issue all
+    # 36 loads of a stage, with at most two stages ahead).  A wait the compiler placed for
+    # Q inside the loop would show up as a count such as 17, 16, ... 1.
+    allowed = {0} | {k * n for n in (3, 4, 5, 6) for k in range(1, 7)} | {9, 18}
     for name, body in _kernels(asm).items():
         waits = set(int(x) for x in re.findall(r"vmcnt\((\d+)\)", body))
         assert waits <= allowed, (name, sorted(waits))
