@@ -9,10 +9,11 @@
 // = floor(j/P) and floor(((jc+r) mod Pc)/c) = j mod P for r < c: the shared
 // block table is the rank-local page table.
 //
-// Kernel shape.  A workgroup of 4 waves owns one (rank, request, KV split,
-// block of 16*RG query rows).  KV is streamed through a 4-stage LDS ring filled
-// by direct-to-LDS 16-byte loads (global_load_lds_dwordx4); every latent row is
-// read from HBM once per workgroup and serves all of its query rows:
+// Kernel shape.  A workgroup of 8 waves owns one (rank, request, KV split,
+// block of 16*RGN query rows).  KV is streamed through an LDS ring of
+// 32-token stages filled by direct-to-LDS 16-byte loads
+// (global_load_lds_dwordx4); every latent row is read from HBM once per
+// workgroup and serves all of its query rows:
 //   S^T[32 tok x 16 rows] = K[32 x 576] . Q^T           (mfma 16x16x32 bf16, K from LDS,
 //                                                       Q^T held in registers)
 //   O^T[512 x 16 rows]   += V^T[512 x 32] . P^T         (V^T read from the same LDS rows
@@ -22,9 +23,6 @@
 // 8g+i with token 4g+i and k-slot 8g+4+i with token 16+4g+i; the transposed V
 // reads supply the same token order.  Every value a lane accumulates belongs
 // to its row j, so the softmax rescale is a per-lane scalar.
-// Waves split the 16*RG rows (RG groups) and, when RG < 4, the 512 output
-// columns (4/RG groups; each such wave recomputes the row's scores, which is
-// cheap for these HBM-bound shapes).
 // Online softmax runs in fp32 in base 2 (scores pre-multiplied by
 // sm_scale*log2 e); the running maximum is only raised when a tile exceeds it
 // by more than kTau, so O is rescaled rarely (any common reference value gives
@@ -40,15 +38,15 @@ namespace dcp {
 
 namespace {
 
-constexpr int kStages = 4;
 constexpr int kWaves = 8;     // waves per workgroup: two per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr float kTau = 8.0f;
 constexpr int kMaxTab = 256;  // page ids staged per workgroup
-#ifndef DCP_SCHED_K
-#define DCP_SCHED_K 6
+// score fragments in token-block-major order (each accumulator then takes its
+// MFMAs back to back) or interleaved
+#ifndef DCP_PC_TBMAJOR
+#define DCP_PC_TBMAJOR 1
 #endif
-constexpr int kSchedK = DCP_SCHED_K;  // k units per scheduling window
 
 struct DecodeParams {
   const uint8_t* pools;
@@ -168,6 +166,14 @@ __device__ __forceinline__ bf16x8 cvt_fp8x8(i32x2 v) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Maximum of three floats in one instruction.  The scores it is used on are
+// never NaN; written as asm because fmaxf would first quiet each operand.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float wave_max_g(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));
   v = fmaxf(v, __shfl_xor(v, 32));
@@ -226,407 +232,25 @@ __device__ __forceinline__ int32_t visible_tokens(int32_t L, int32_t r, int32_t 
   return n < n_r ? n : n_r;
 }
 
-template <int RG, bool FP8, bool ALIGNED>
-__global__ void __launch_bounds__(kThreads, 1) mla_decode_kernel(DecodeParams p) {
-  constexpr int SUB = kWaves / RG;        // waves per row group
-  constexpr int NKP = SUB / 2;            // k-parts of the score product per token block
-  constexpr int MB = 16 * RG;             // query rows per workgroup
-  constexpr int ROWB = FP8 ? kDqk : 2 * kDqk;
-  constexpr int CH = ROWB / 16;           // 16-byte chunks per latent row
-  constexpr int STOK = FP8 ? 64 : 32;     // tokens per stage
-  constexpr int NSUB = STOK / 32;         // 32-token sub-tiles per stage
-  constexpr int SBYTES = STOK * ROWB;     // 36864 either way
-  constexpr int NI_ALL = SBYTES / 1024;   // 1 KB direct-to-LDS loads per stage
-  constexpr int NI_MAX = (NI_ALL + kWaves - 1) / kWaves;
-  constexpr int NDB = 32 / kWaves;        // 16-column output blocks per wave (all row groups)
-  constexpr int KU = FP8 ? 9 : 18;        // k units: bf16 k-steps, or e4m3 k-step pairs
-  constexpr int KUW = (KU + NKP - 1) / NKP;  // most k units one wave handles
-  constexpr int NQF = FP8 ? 2 * KUW : KUW;   // Q^T fragments held by a wave
-  static_assert(RG == 1 || RG == 2 || RG == 4, "row groups");
-  static_assert(NI_ALL % 4 == 0 && NI_ALL / kWaves + 1 == NI_MAX, "load split");
-
-  // Stage ring.  The direct-to-LDS loads that fill it are issued from inline
-  // asm (dma_* below), so the compiler does not see them as pending LDS
-  // writes and inserts no vector-memory waits before the ring's LDS reads;
-  // the explicit vmcnt waits and barriers in step() order them instead.
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv[kStages * SBYTES];
-  __shared__ __attribute__((aligned(16))) float lds_sc[FP8 ? kStages * STOK : 4];
-  __shared__ __attribute__((aligned(16))) f32x4 lds_xch[kWaves * 64];  // partial S^T blocks
-  __shared__ int32_t lds_pt[kMaxTab];
-  __shared__ __attribute__((aligned(16))) bf16x8 lds_p[RG * 64];  // P^T operand of each row group
-  __shared__ float lds_alpha[RG * 16];                           // rescale factor per row
-  __shared__ float lds_l[RG * 16];                               // final normaliser per row
-  __shared__ int lds_resc[RG];                                   // tile whose P needs a rescale
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, j = lane & 15;
-  const int rg = w / SUB, sw = w % SUB;
-  const int tb = sw & 1, kp = sw >> 1;      // score slice: token block, k part
-  const int ku0 = KU * kp / NKP, nku = KU * (kp + 1) / NKP - ku0;
-
-  // XCD-aware unit mapping: the row blocks of one (rank, request, split) sit on
-  // the same XCD (ids congruent mod 8) so their KV reads share that L2.
-  const WgUnit wu = wg_unit(blockIdx.x, p.n_row_blocks);
-  const int rb = wu.rb;
-  const int64_t unit = wu.unit;
-  if (unit >= p.units_total) return;
-  const int split = (int)(unit % p.splits);
-  const int64_t rbu = unit / p.splits;
-  const int b = (int)(rbu % p.batch);
-  const int rl = (int)(rbu / p.batch);
-  const int64_t r = (int64_t)p.rank_begin + rl;
-  const int64_t c = p.c, P = p.page;
-
-  const int row0 = rb * MB + rg * 16;     // first query row of this wave's row group
-  const int64_t orow = (((int64_t)rl * p.batch + b) * p.splits + split) * p.rows + row0 + j;
-
-  const int32_t L = request_len(p, b, tid == 0);
-
-  // all rank-local token indices fit in int32 (seq_len is int32)
-  const int32_t ri = (int32_t)r, Pi = (int32_t)P;
-  auto visible = [&](int qi) -> int32_t { return visible_tokens(L, ri, p.c, p.q_len, qi, p.causal); };
-  const int32_t split_tok = (int32_t)p.split_tokens;
-  const int32_t j_begin = split * split_tok;
-  const int32_t n_wg = visible((rb * MB + MB - 1) / p.heads);
-  const int32_t j_end = min(n_wg, j_begin + split_tok);
-  const int32_t jlim = min(visible(row0 / p.heads), j_begin + split_tok);
-  const int n_st = j_end > j_begin ? (j_end - j_begin + STOK - 1) / STOK : 0;
-  // a split past the end of every row of the block writes nothing (the split
-  // combine reads only the splits that hold visible tokens of a row); split 0
-  // always writes, so that an empty shard still yields lse = -inf and o = 0
-  if (n_st == 0 && split > 0) return;
-
-  const uint8_t* pool = p.pools + (int64_t)rl * p.pool_bytes;
-  const float* spool = FP8 ? p.pool_scales + (int64_t)rl * p.cap : nullptr;
-  const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
-
-  // Page ids of this split, staged once in LDS so that the load pipeline below
-  // never waits on a vector-memory result.  Invalid ids are reported and
-  // replaced by page 0 so that every access stays inside the pool.
-  const int32_t vp_first = j_begin / Pi;
-  const int32_t n_tab = n_st > 0 ? (j_end - 1) / Pi - vp_first + 1 : 0;  // <= kMaxTab by the plan
-  {
-    bool bad_page = false;
-    for (int t = tid; t < n_tab; t += kThreads) {
-      int32_t pg = bt[vp_first + t];
-      if ((unsigned)pg >= (unsigned)p.num_pages) {
-        bad_page = true;
-        pg = 0;
-      }
-      lds_pt[t] = pg;
-    }
-    if (bad_page && p.dev_status) atomicMax(p.dev_status, DCP_DEV_BAD_PAGE);
-  }
-
-  // Q^T operand of this wave's score slice (rows row0..row0+15, k units
-  // [ku0, ku0+nku)).  bf16: unit u is k-step u and lane (g, j) holds
-  // q[row0+j][32u+8g .. +8].  e4m3: unit u is the k-step pair read with one
-  // 16-byte K load, fragment 2i+e holds q[row0+j][64u+16g+8e .. +8]; any order
-  // of the 576 columns gives the same dot product when K and Q agree.
-  bf16x8 qf[NQF];
-  {
-    const uint16_t* qrow = p.q + ((int64_t)b * p.rows + row0 + j) * kDqk;
-#pragma unroll
-    for (int i = 0; i < KUW; ++i) {
-      const int u = min(ku0 + i, KU - 1);
-      if (FP8) {
-        qf[2 * i] = *reinterpret_cast<const bf16x8*>(qrow + 64 * u + 16 * g);
-        qf[2 * i + 1] = *reinterpret_cast<const bf16x8*>(qrow + 64 * u + 16 * g + 8);
-      } else {
-        qf[i] = *reinterpret_cast<const bf16x8*>(qrow + 32 * u + 8 * g);
-      }
-    }
-  }
-  // Q (and the page table) must have landed before the loop: the compiler
-  // does not count the asm loads below, so a wait for Q placed inside the
-  // loop would also drain every load in flight.
-  wait_vmcnt<0>();
-  __syncthreads();  // page table visible
-
-  // ---- direct-to-LDS loads of one stage.  Wave w issues loads w, w+8, ... of
-  // the stage's NI_ALL; load i fills LDS bytes [1024 i, 1024 i + 1024), lane k
-  // the 16 bytes at 1024 i + 16 k, which hold chunk (pos ^ swz(row)) of stage
-  // row `row` (pos = position inside the row).
-  const int ni = (w < NI_ALL % kWaves) ? NI_MAX : NI_MAX - 1;  // loads this wave issues
-  int dma_row[NI_MAX];        // stage row (token) each load of this lane fetches
-  uint32_t dma_off[NI_MAX];   // its byte offset from the stage's first row
-#pragma unroll
-  for (int t = 0; t < NI_MAX; ++t) {
-    const int ci = (w + kWaves * t) * 64 + lane;
-    const int row = min(ci / CH, STOK - 1);
-    dma_row[t] = row;
-    dma_off[t] = (uint32_t)(row * ROWB + ((ci % CH) ^ swz<FP8>(row)) * 16);
-  }
-  const int32_t jb_off = j_begin - vp_first * Pi;  // offset of j_begin inside its page
-  auto slot_of = [&](int32_t jj) -> int64_t {
-    const int32_t pidx = jj / Pi;
-    return (int64_t)lds_pt[pidx - vp_first] * Pi + (jj - pidx * Pi);
-  };
-  auto issue = [&](int s) {
-    uint8_t* dst = lds_kv + (s % kStages) * SBYTES;
-    float* dst_sc = lds_sc + (FP8 ? (s % kStages) * STOK : 0);
-    const int32_t j0 = j_begin + s * STOK;
-    if (ALIGNED && j0 + STOK <= j_end) {
-      // whole stage inside one page: one page id, fixed per-lane offsets
-      const int32_t rel = jb_off + s * STOK;
-      const int32_t pidx = rel / Pi;
-      const int32_t pg = __builtin_amdgcn_readfirstlane(lds_pt[pidx]);
-      const int64_t slot0 = (int64_t)pg * Pi + (rel - pidx * Pi);
-      const uint8_t* base = pool + slot0 * ROWB;
-#pragma unroll
-      for (int t = 0; t < NI_MAX; ++t)
-        if (t < ni) dma16(base, dma_off[t], dst + (w + kWaves * t) * 1024);
-      if (FP8 && lane < 8) dma4_abs(spool + slot0 + 8 * w + lane, dst_sc + 8 * w);
-    } else {
-      // last stage of a split (rows past j_end repeat the last valid row) or
-      // pages that a stage can straddle
-#pragma unroll
-      for (int t = 0; t < NI_MAX; ++t)
-        if (t < ni) {
-          const int32_t jj = min(j0 + dma_row[t], j_end - 1);
-          dma16_abs(pool + slot_of(jj) * ROWB + (dma_off[t] - dma_row[t] * ROWB), dst + (w + kWaves * t) * 1024);
-        }
-      if (FP8) {
-        const int32_t jj = min(j0 + 8 * w + (lane & 7), j_end - 1);
-        const float* src = spool + slot_of(jj);
-        if (lane < 8) dma4_abs(src, dst_sc + 8 * w);
-      }
-    }
-  };
-
-  // Per-lane LDS byte offsets (swizzled) of the K and transposed-V reads.
-  // K (A operand of S^T): row 16*tb + j (+32*sub for e4m3), 16-byte chunk
-  // 4*u + g.
-  // bf16 V^T: ds_read_b64_tr_b16 lane k reads row 16*h + 4*(k>>4) + ((k>>2)&3),
-  // 8 bytes at column block db: chunk 2*db + ((k&3)>>1), half k&1.
-  // e4m3 V^T: ds_read_b64_tr_b8 lane k = 16G + 2s + q reads row tok(G, s) with
-  // tok = 4G+s (s<4) or 16+4G+s-4, chunk db, half q.
-  int koff[2], voff[2][4];
-  if (!FP8) {
-    // k-step u of row `row` sits at byte row*ROWB + 128*(u>>1) + 16*((4*(u&1)+g) ^ swz(row)):
-    // koff[e] is the offset of the wave's k-step ku0+e, and k-step ku0+e+2t lies 128*t further
-    const int row = 16 * tb + j;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int u = ku0 + e;
-      koff[e] = row * ROWB + 128 * (u >> 1) + 16 * ((4 * (u & 1) + g) ^ swz<false>(row));
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int vrow = 16 * h + 4 * (lane >> 4) + ((lane >> 2) & 3);
-      const int y = ((lane & 3) >> 1) ^ swz<false>(vrow);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) voff[h][m] = vrow * ROWB + 16 * ((2 * m) ^ y) + 8 * (lane & 1);
-    }
-  } else {
-    const int s8 = (lane & 15) >> 1;
-    const int trow = s8 < 4 ? 4 * (lane >> 4) + s8 : 16 + 4 * (lane >> 4) + (s8 - 4);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int row = 32 * sub + 16 * tb + j;
-      koff[sub] = row * ROWB + 64 * ku0 + 16 * (g ^ swz<true>(row));
-      const int vrow = 32 * sub + trow;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) voff[sub][m] = vrow * ROWB + 16 * (m ^ swz<true>(vrow)) + 8 * (lane & 1);
-    }
-  }
-
-  // O^T accumulators: this wave's NDB output blocks for every row group.
-  f32x4 acc[NDB][RG];
-#pragma unroll
-  for (int d = 0; d < NDB; ++d)
-#pragma unroll
-    for (int q = 0; q < RG; ++q) acc[d][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // softmax state of row row0 + j (every wave of a row group keeps identical copies)
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4* xch_mine = lds_xch + w * 64 + lane;
-  const f32x4* xch_grp = lds_xch + rg * SUB * 64 + lane;
-  if (tid < RG) lds_resc[tid] = -1;
-  int tile_no = 0;
-
-  // One 32-token sub-tile of a resident stage.
-  auto tile = [&](const uint8_t* kv, const float* sc, int sub, int32_t jt) {
-    // ---- this wave's slice of S^T: token block tb, k units [ku0, ku0+nku)
-    f32x4 sp = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < KUW; ++i) {
-      // bound how far the scheduler hoists K loads ahead of their MFMAs
-      if (i % kSchedK == 0 && i > 0) __builtin_amdgcn_sched_barrier(0);
-      if (i < nku) {
-        const int u = ku0 + i;
-        if (FP8) {
-          const i32x4 raw = *reinterpret_cast<const i32x4*>(kv + koff[sub] + 64 * i);
-          sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{raw[0], raw[1]}), qf[2 * i], sp, 0, 0, 0);
-          sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{raw[2], raw[3]}), qf[2 * i + 1], sp, 0, 0, 0);
-        } else {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kv + koff[i & 1] + 128 * (i >> 1));
-          sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i], sp, 0, 0, 0);
-        }
-      }
-    }
-    // ---- exchange the slices of the row group; sum the k parts
-    *xch_mine = sp;
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slice is in LDS
-    wg_barrier();
-    f32x4 sacc[2];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      sacc[t2] = xch_grp[t2 * 64];
-#pragma unroll
-      for (int k2 = 1; k2 < NKP; ++k2) sacc[t2] += xch_grp[(t2 + 2 * k2) * 64];
-    }
-    // ---- online softmax (base 2), lane holds tokens t2*16 + 4g + i of row j.
-    // The running maximum only moves when some score exceeds it by kTau; that
-    // is detected with a ballot and only then is the row maximum formed
-    // across the lanes of the row.
-    const int tb0 = 32 * sub;
-    float sv[8], tsc[8];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t2 * 16 + 4 * g + i;
-        float x = sacc[t2][i] * p.scale_log2;
-        if (FP8) {
-          tsc[t2 * 4 + i] = sc[tb0 + t];
-          x *= tsc[t2 * 4 + i];
-        }
-        x = (jt + t < jlim) ? x : -INFINITY;
-        sv[t2 * 4 + i] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    }
-    float alpha = 1.f;
-    const bool resc = __any(mloc > m_run + kTau);  // also true on the first visible tile
-    if (resc) {
-      const float mt = wave_max_g(mloc);
-      if (mt > m_run + kTau) {
-        alpha = exp2f(m_run - mt);
-        m_run = mt;
-      }
-    }
-    const float mref = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
-    bf16x8 pf;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float pe = exp2f(sv[e] - mref);
-      psum += pe;
-      if (FP8) pe *= tsc[e];
-      pf[e] = (__bf16)pe;
-    }
-    l_run = l_run * alpha + psum;
-    if (sw == 0) {  // one wave per row group publishes P^T (and the rescale factors)
-      lds_p[rg * 64 + lane] = pf;
-      if (resc) {
-        if (g == 0) lds_alpha[rg * 16 + j] = alpha;
-        if (lane == 0) lds_resc[rg] = tile_no;
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P^T is in LDS
-    wg_barrier();
-    // ---- O^T += V^T . P^T for this wave's output blocks, every row group
-    bf16x8 pg[RG];
-#pragma unroll
-    for (int q = 0; q < RG; ++q) {
-      pg[q] = lds_p[q * 64 + lane];
-      if (lds_resc[q] == tile_no) {
-        const float a = lds_alpha[q * 16 + j];
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) acc[d][q] *= a;
-      }
-    }
-    ++tile_no;
-#pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      const int db = w * NDB + d;
-      bf16x8 a;
-      if (FP8) {
-        i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(DCP_LDS(i32x2, kv + voff[sub][db & 3] + 64 * (db >> 2)));
-        a = cvt_fp8x8(raw);
-      } else {
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DCP_LDS(i16x4, kv + voff[0][db & 3] + 128 * (db >> 2)));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DCP_LDS(i16x4, kv + voff[1][db & 3] + 128 * (db >> 2)));
-        typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
-        i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        a = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int q = 0; q < RG; ++q) acc[d][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pg[q], acc[d][q], 0, 0, 0);
-    }
-  };
-
-  // One ring step: wait for stage s, refill the stage computed one step ago,
-  // then compute stage s.  Barriers are uniform across the workgroup.
-  for (int s = 0; s < kStages - 1 && s < n_st; ++s) issue(s);
-  for (int s = 0; s < n_st; ++s) {
-    const int ahead = min(kStages - 2, n_st - 1 - s);
-    if (w < NI_ALL % kWaves) {
-      constexpr int NV = NI_MAX + (FP8 ? 1 : 0);
-      if (ahead >= 2) wait_vmcnt<2 * NV>();
-      else if (ahead == 1) wait_vmcnt<NV>();
-      else wait_vmcnt<0>();
-    } else {
-      constexpr int NV = NI_MAX - 1 + (FP8 ? 1 : 0);
-      if (ahead >= 2) wait_vmcnt<2 * NV>();
-      else if (ahead == 1) wait_vmcnt<NV>();
-      else wait_vmcnt<0>();
-    }
-    wg_barrier();
-    if (s + kStages - 1 < n_st) issue(s + kStages - 1);
-    const uint8_t* kv = lds_kv + (s % kStages) * SBYTES;
-    const float* sc = lds_sc + (FP8 ? (s % kStages) * STOK : 0);
-    const int32_t j0 = j_begin + s * STOK;
-    tile(kv, sc, 0, j0);
-    // The second e4m3 sub-tile reuses the exchange and P^T buffers: every wave
-    // read the slices before the P^T barrier and finished its PV before the
-    // next slice barrier, so no extra barrier is needed.
-    if (NSUB == 2 && j0 + 32 < j_end) tile(kv, sc, 1, j0 + 32);
-  }
-
-  // ---- finalise: o = O / l, lse = m + log2(l) (then base conversion)
-  const float l_tot = wave_sum_g(l_run);
-  if (sw == 0) {
-    if (g == 0) {
-      lds_l[rg * 16 + j] = l_tot;
-      const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
-      p.lse_out[orow] = p.out_base2 ? lse2 : lse2 * kLn2;
-    }
-  }
-  __syncthreads();
-  const int64_t orow0 = (((int64_t)rl * p.batch + b) * p.splits + split) * p.rows + rb * MB + j;
-#pragma unroll
-  for (int q = 0; q < RG; ++q) {
-    const float lq = lds_l[q * 16 + j];
-    const float inv = lq > 0.f ? 1.0f / lq : 0.f;
-    float* optr = p.o_out + (orow0 + q * 16) * kDv;
-#pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      const int col = (w * NDB + d) * 16 + 4 * g;
-      *reinterpret_cast<f32x4*>(optr + col) = acc[d][q] * inv;
-    }
-  }
-}
-
-// Producer/consumer variant for workgroups of 64 query rows (4 row blocks).
-// Waves 0-3 (one per SIMD) produce: wave q owns row block q, computes its full
-// S^T (both 16-token blocks, all 576 columns), the online softmax and P^T,
-// and publishes P^T (with the rescale factors when the running maximum
-// moved) in a double-buffered LDS area.  Waves 4-7 consume: wave 4+c owns
-// output columns [128c, 128c+128) of all 64 rows and multiplies V^T by the P^T
-// of the previous tile, so each transposed V fragment feeds four MFMAs.  One
+// Decode kernel: a workgroup of 8 waves owns RGN row blocks of 16 query rows
+// (RGN = 4, 2 or 1).  Waves 0..RGN-1 produce: wave q owns row block q,
+// computes its full S^T (both 16-token blocks, all 576 columns), the online
+// softmax and P^T, and publishes P^T (with the rescale factors when the
+// running maximum moved) in a double-buffered LDS area.  Waves 4-7 consume:
+// wave 4+c owns output columns [128c, 128c+128) of every row block and
+// multiplies V^T by the P^T of the previous tile, so each transposed V
+// fragment feeds RGN MFMAs; waves RGN..3 (RGN < 4) only take part in the
+// barriers.  One
 // workgroup barrier per tile hands P^T over and recycles the stage the
 // consumers finished; producer and consumer of a SIMD run different phases
 // and overlap.  Producers run at a raised wave priority, so their MFMAs go
 // first and the consumer's MFMAs fill the time of the producer's softmax;
 // the consumers also issue every direct-to-LDS load, which keeps the
 // producers' path from one barrier to the next free of load issue and waits.
-template <bool FP8, bool ALIGNED>
+template <int RGN, bool FP8, bool ALIGNED>
 __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams p) {
-  constexpr int RGN = 4;                  // row blocks per workgroup
-  constexpr int MB = 16 * RGN;
+  static_assert(RGN == 1 || RGN == 2 || RGN == 4, "row blocks per workgroup");
+  constexpr int MB = 16 * RGN;            // query rows per workgroup
   constexpr int ROWB = FP8 ? kDqk : 2 * kDqk;
   constexpr int CH = ROWB / 16;
   constexpr int STOK = 32;                // tokens per stage (one tile)
@@ -644,7 +268,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   __shared__ int32_t lds_pt[kMaxTab];
   __shared__ __attribute__((aligned(16))) bf16x8 lds_p[2][RGN * 64];
   __shared__ float lds_alpha[2][RGN * 16];
-  __shared__ __attribute__((aligned(16))) int lds_resc[2][RGN];
+  __shared__ __attribute__((aligned(16))) int lds_resc[2][4];  // read as one 16-byte vector
   __shared__ float lds_l[RGN * 16];
 
   const int tid = threadIdx.x;
@@ -675,6 +299,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   const int32_t n_wg = visible((rb * MB + MB - 1) / p.heads);
   const int32_t j_end = min(n_wg, j_begin + split_tok);
   const int32_t jlim = min(visible(row0 / p.heads), j_begin + split_tok);
+  // wave-uniform: every row of a 16-row block belongs to the same query index
+  const int32_t jlim_s = __builtin_amdgcn_readfirstlane(jlim);
   const int n_st = j_end > j_begin ? (j_end - j_begin + STOK - 1) / STOK : 0;
   // a split past the end of every row of the block writes nothing (the split
   // combine reads only the splits that hold visible tokens of a row); split 0
@@ -698,12 +324,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     }
     if (bad_page && p.dev_status) atomicMax(p.dev_status, DCP_DEV_BAD_PAGE);
   }
-  if (tid < 2 * RGN) lds_resc[tid / RGN][tid % RGN] = -1;
+  if (tid < 8) lds_resc[tid >> 2][tid & 3] = -1;
 
   // One register array serves both roles, which are fixed per wave: a
   // producer keeps its Q^T fragments (18 x 16 bytes) in R[0..17], a consumer
   // its O^T accumulators (8 blocks x 4 row blocks) in R[0..31].
-  f32x4 R[NDBC * RGN];
+  constexpr int NR = NDBC * RGN > 18 ? NDBC * RGN : 18;
+  f32x4 R[NR];
   if (producer) {
     const uint16_t* qrow = p.q + ((int64_t)b * p.rows + row0 + j) * kDqk;
 #pragma unroll
@@ -713,10 +340,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < NDBC * RGN; ++i) R[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NR; ++i) R[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   auto qf = [&](int kk) { return __builtin_bit_cast(bf16x8, R[kk]); };
-  wait_vmcnt<0>();  // Q and the page table have landed (see mla_decode_kernel)
+  // Q and the page table must have landed before the loop: the compiler does
+  // not count the asm loads below, so a wait for Q placed inside the loop
+  // would also drain every load in flight
+  wait_vmcnt<0>();
   __syncthreads();
 
   // direct-to-LDS loads, issued by the consumer waves: loading wave lw issues
@@ -817,13 +447,14 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     if (FP8) {
       constexpr int NF = 2 * KU, PD = 6;
       i32x4 kf[NF];
-      auto kload = [&](int f) { return *reinterpret_cast<const i32x4*>(kv + koff[f & 1][0] + 64 * (f >> 1)); };
+      // fragment f = KU*tb + u (token-block major, as for bf16)
+      auto kload = [&](int f) { return *reinterpret_cast<const i32x4*>(kv + koff[f / KU][0] + 64 * (f % KU)); };
 #pragma unroll
       for (int f = 0; f < PD; ++f) kf[f] = kload(f);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         if (f + PD < NF) kf[f + PD] = kload(f + PD);
-        const int u = f >> 1, tb = f & 1;
+        const int u = f % KU, tb = f / KU;
         sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{kf[f][0], kf[f][1]}), qf(2 * u), sacc[tb], 0, 0, 0);
         sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{kf[f][2], kf[f][3]}), qf(2 * u + 1), sacc[tb], 0, 0, 0);
       }
@@ -835,18 +466,21 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * PD, 0);
     } else {
+      // fragment f = KU*tb + u: each accumulator takes its 18 MFMAs back to back
       constexpr int NF = 2 * KU, PD = 8;
       bf16x8 kf[NF];
+      auto ftb = [](int f) { return DCP_PC_TBMAJOR ? f / KU : f & 1; };
+      auto fu = [](int f) { return DCP_PC_TBMAJOR ? f % KU : f >> 1; };
       auto kload = [&](int f) {
-        const int u = f >> 1;
-        return *reinterpret_cast<const bf16x8*>(kv + koff[f & 1][u & 1] + 128 * (u >> 1));
+        const int tb = ftb(f), u = fu(f);
+        return *reinterpret_cast<const bf16x8*>(kv + koff[tb][u & 1] + 128 * (u >> 1));
       };
 #pragma unroll
       for (int f = 0; f < PD; ++f) kf[f] = kload(f);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         if (f + PD < NF) kf[f + PD] = kload(f + PD);
-        sacc[f & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f], qf(f >> 1), sacc[f & 1], 0, 0, 0);
+        sacc[ftb(f)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f], qf(fu(f)), sacc[ftb(f)], 0, 0, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
 #pragma unroll
@@ -856,30 +490,35 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
       }
       __builtin_amdgcn_sched_group_barrier(0x008, PD, 0);
     }
-    float sv[8], tsc[8];
-    float mloc = -INFINITY;
-    const bool whole = jt + STOK <= jlim;  // every token of the tile visible to this row block
+    // ---- online softmax (base 2); lane holds tokens t2*16 + 4g + i of row j.
+    // The running maximum only moves when some score exceeds it by kTau; that
+    // is detected with a ballot and only then is the row maximum formed
+    // across the lanes of the row.  exp2 is the hardware instruction: a
+    // probability below 2^-126 flushes to zero, far below what bf16 P keeps.
+    float y[8], tsc[8];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tk = t2 * 16 + 4 * g + i;
-        float x = sacc[t2][i] * p.scale_log2;
-        if (FP8) {
-          tsc[t2 * 4 + i] = sc[tk];
-          x *= tsc[t2 * 4 + i];
-        }
-        if (!whole) x = (jt + tk < jlim) ? x : -INFINITY;
-        sv[t2 * 4 + i] = x;
-        mloc = fmaxf(mloc, x);
+    for (int e = 0; e < 8; ++e) {
+      y[e] = sacc[e >> 2][e & 3];
+      if (FP8) {
+        tsc[e] = sc[(e >> 2) * 16 + 4 * g + (e & 3)];
+        y[e] *= tsc[e];
       }
+      y[e] *= p.scale_log2;
     }
+    if (jt + STOK > jlim_s) {  // the tile reaches past this row block's last visible token
+      // masked by adding -inf, so every y stays an arithmetic result (the max
+      // below then needs no NaN canonicalisation)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        y[e] += (jt + (e >> 2) * 16 + 4 * g + (e & 3) >= jlim_s) ? -INFINITY : 0.f;
+    }
+    float mloc = max3f(max3f(y[0], y[1], y[2]), max3f(y[3], y[4], y[5]), fmaxf(y[6], y[7]));
     float alpha = 1.f;
     const bool resc = __any(mloc > m_run + kTau);
     if (resc) {
       const float mt = wave_max_g(mloc);
       if (mt > m_run + kTau) {
-        alpha = exp2f(m_run - mt);
+        alpha = __builtin_amdgcn_exp2f(m_run - mt);
         m_run = mt;
       }
     }
@@ -888,7 +527,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     bf16x8 pf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float pe = exp2f(sv[e] - mref);
+      float pe = __builtin_amdgcn_exp2f(y[e] - mref);
       psum += pe;
       if (FP8) pe *= tsc[e];
       pf[e] = (__bf16)pe;
@@ -925,7 +564,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
         vf[d] = __builtin_bit_cast(bf16x8, v);
       }
     }
-    if (resc[0] == t || resc[1] == t || resc[2] == t || resc[3] == t) {
+    bool any_resc = false;
+#pragma unroll
+    for (int q = 0; q < RGN; ++q) any_resc |= resc[q] == t;
+    if (any_resc) {
 #pragma unroll
       for (int q = 0; q < RGN; ++q)
         if (resc[q] == t) {
@@ -1020,21 +662,13 @@ split_combine_kernel(DecodeParams p, const float* __restrict__ ws_o, const float
   if (col4 == 0) lse_part[row] = out_base2 ? lse2 : lse2 * kLn2;
 }
 
-template <int RG, bool FP8, bool ALIGNED>
-hipError_t launch_variant(const DecodeParams& prm, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_decode_kernel<RG, FP8, ALIGNED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, prm);
+template <int RGN, bool FP8>
+hipError_t launch_pc(const DecodeParams& prm, bool aligned, int64_t grid, hipStream_t stream) {
+  if (aligned)
+    hipLaunchKernelGGL((mla_decode_pc_kernel<RGN, FP8, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, prm);
+  else
+    hipLaunchKernelGGL((mla_decode_pc_kernel<RGN, FP8, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, prm);
   return hipGetLastError();
-}
-
-template <bool FP8, bool ALIGNED>
-hipError_t launch_pc(const DecodeParams& prm, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_decode_pc_kernel<FP8, ALIGNED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, prm);
-  return hipGetLastError();
-}
-
-template <int RG, bool FP8>
-hipError_t launch_rg(const DecodeParams& prm, bool aligned, int64_t grid, hipStream_t s) {
-  return aligned ? launch_variant<RG, FP8, true>(prm, grid, s) : launch_variant<RG, FP8, false>(prm, grid, s);
 }
 
 }  // namespace
@@ -1058,7 +692,7 @@ DecodePlan plan_decode(int32_t c, int32_t page, bool fp8, int32_t rank_count, in
   const int rg = pl.rows % 64 == 0 ? 4 : (pl.rows % 32 == 0 ? 2 : 1);
   pl.row_block = 16 * rg;
   pl.n_row_blocks = pl.rows / pl.row_block;
-  pl.stage_tokens = (fp8 && rg < 4) ? 64 : 32;  // the 64-row kernel streams 32-token stages
+  pl.stage_tokens = 32;
   const int64_t n_r_max = (max_seq_len + c - 1) / c;
   const int64_t stages_max = (n_r_max + pl.stage_tokens - 1) / pl.stage_tokens;
   const int64_t units = (int64_t)rank_count * batch * pl.n_row_blocks;
@@ -1128,16 +762,12 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   const int64_t grid = (prm.units_total + 7) / 8 * 8 * pl.n_row_blocks;
   hipError_t e;
   const int rg = pl.row_block / 16;
-  if (rg == 4) {
-    if (a.fp8)
-      e = aligned ? launch_pc<true, true>(prm, grid, stream) : launch_pc<true, false>(prm, grid, stream);
-    else
-      e = aligned ? launch_pc<false, true>(prm, grid, stream) : launch_pc<false, false>(prm, grid, stream);
-  } else if (a.fp8) {
-    e = rg == 2 ? launch_rg<2, true>(prm, aligned, grid, stream) : launch_rg<1, true>(prm, aligned, grid, stream);
-  } else {
-    e = rg == 2 ? launch_rg<2, false>(prm, aligned, grid, stream) : launch_rg<1, false>(prm, aligned, grid, stream);
-  }
+  if (a.fp8)
+    e = rg == 4 ? launch_pc<4, true>(prm, aligned, grid, stream)
+                : (rg == 2 ? launch_pc<2, true>(prm, aligned, grid, stream) : launch_pc<1, true>(prm, aligned, grid, stream));
+  else
+    e = rg == 4 ? launch_pc<4, false>(prm, aligned, grid, stream)
+                : (rg == 2 ? launch_pc<2, false>(prm, aligned, grid, stream) : launch_pc<1, false>(prm, aligned, grid, stream));
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t n_rows_total = (int64_t)a.rank_count * a.batch * pl.rows;
   hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)((n_rows_total + 1) / 2)), dim3(256), 0, stream, prm,

@@ -43,7 +43,8 @@ def test_m0_only_feeds_lds_dma(asm):
 
 def test_decode_kernels_do_not_spill(asm):
     ks = _kernels(asm)
-    assert len(ks) == 12 and sum("pc_kernel" in k for k in ks) == 4
+    # 1, 2 or 4 row blocks x bf16/e4m3 x page-aligned or not
+    assert len(ks) == 12 and all("pc_kernel" in k for k in ks)
     for name, body in ks.items():
         assert "scratch_" not in body, name
 
