@@ -150,7 +150,10 @@ int dcp_kv_write(const dcp_layout* layout, void* pools, float* pool_scales,
 
 /*
  * mla_decode_workspace_size - bytes of workspace mla_decode_partial needs for
- * these sizes (0 if none).  max_seq_len bounds every seq_len[b].
+ * these sizes (0 only for invalid arguments).  max_seq_len bounds every
+ * seq_len[b].  The workspace holds the call's work plan (how each (rank,
+ * request) is cut into KV splits, decided on the device from seq_len) and
+ * the partial outputs of requests that are split.
  */
 size_t mla_decode_workspace_size(const dcp_layout* layout, int32_t rank_count, int32_t batch,
                                  int32_t q_len, int32_t heads, int64_t max_seq_len);
@@ -184,7 +187,8 @@ size_t mla_decode_workspace_size(const dcp_layout* layout, int32_t rank_count, i
  *   o_part       float32 [rank_count][batch][q_len][heads][512]
  *   lse_part     float32 [rank_count][batch][q_len][heads]
  *   workspace    device scratch of at least mla_decode_workspace_size(...)
- *                bytes (may be NULL if that size is 0); contents are scratch
+ *                bytes, 16-byte aligned; contents are scratch, and calls that
+ *                share one workspace must not overlap in time
  */
 int mla_decode_partial(const dcp_layout* layout, const void* pools, const float* pool_scales,
                        int32_t rank_begin, int32_t rank_count, const void* q, int32_t batch,

@@ -21,15 +21,21 @@ hipError_t launch_kv_write(int32_t c, int32_t page, int32_t num_pages, bool fp8,
 hipError_t launch_lse_merge(int32_t c, int64_t rows, const float* o_part, const float* lse_part,
                             bool base2, void* o_out, float* lse_out, hipStream_t stream);
 
-// Work decomposition of one mla_decode_partial call.
+// Work decomposition of one mla_decode_partial call.  The split of each
+// (rank, request) into work items is planned on the device at every call;
+// the host fixes the row blocking and bounds the number of items.
 struct DecodePlan {
   int32_t rows;            // q_len * heads
   int32_t row_block;       // query rows per workgroup (16, 32 or 64)
   int32_t n_row_blocks;    // rows / row_block
   int32_t stage_tokens;    // tokens per LDS stage
-  int32_t splits;          // KV splits per (rank, request)
-  int64_t split_tokens;    // rank-local tokens per split (multiple of stage_tokens)
-  size_t workspace_bytes;  // 0 when splits == 1
+  int64_t units;           // rank_count * batch
+  int32_t items_target;    // work items per row block the device plan aims for
+  int32_t t_min, t_max;    // item length bounds in stages
+  int64_t max_items;       // bound on the items the device plan makes
+  size_t off_ws_lse;       // workspace: partial o, then partial lse, then the plan
+  size_t off_ints;
+  size_t workspace_bytes;
 };
 
 DecodePlan plan_decode(int32_t c, int32_t page, bool fp8, int32_t rank_count, int32_t batch, int32_t q_len,

@@ -41,7 +41,8 @@ namespace {
 constexpr int kWaves = 8;     // waves per workgroup: two per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr float kTau = 8.0f;
-constexpr int kMaxTab = 256;  // page ids staged per workgroup
+constexpr int kMaxTab = 512;  // page ids staged per workgroup
+constexpr int kStageTok = 32; // tokens per LDS stage
 // score fragments in token-block-major order (each accumulator then takes its
 // MFMAs back to back) or interleaved
 #ifndef DCP_PC_TBMAJOR
@@ -61,14 +62,25 @@ struct DecodeParams {
   const int32_t* seq_len;
   int64_t max_seq_len;
   float scale_log2;  // sm_scale * log2(e)
-  int32_t out_base2;  // lse written in base 2 (else base e)
+  int32_t out_base2;  // lse_part in base 2 (else base e)
   int32_t causal;
-  float* o_out;    // [rank][batch][splits][rows][512]
-  float* lse_out;  // [rank][batch][splits][rows]
-  int32_t splits;
-  int64_t split_tokens;
+  float* o_part;    // [units][rows][512], unit = rank * batch + request
+  float* lse_part;  // [units][rows]
   int32_t n_row_blocks;
-  int64_t units_total;
+  int32_t units;    // rank_count * batch
+  // work plan (written each call by decode_plan_kernel, in the workspace)
+  int32_t max_items;
+  int32_t items_target;  // work items per row block the plan aims for
+  int32_t t_min, t_max;  // bounds of an item's length in stages
+  int32_t* n_items;      // [2]: work items, split units
+  int32_t* item_unit;    // [max_items]
+  int32_t* item_jb;      // [max_items] first rank-local token of the item
+  int32_t* item_je;      // [max_items] end of the item's tokens
+  int32_t* unit_first;   // [units] first item of the unit
+  int32_t* unit_count;   // [units] items of the unit
+  int32_t* split_units;  // [units] the units with several items
+  float* ws_o;           // [max_items][rows][512] partials of units with several items
+  float* ws_lse;         // [max_items][rows] (base 2)
   int32_t* dev_status;
 };
 
@@ -188,10 +200,10 @@ __device__ __forceinline__ float wave_sum_g(float v) {
 
 // Workgroup -> (row block, work unit).  Workgroup ids congruent mod 8 run on
 // the same XCD; the row blocks of one unit get ids congruent mod 8 so their KV
-// reads share that XCD's L2.  Each block of 8 consecutive units is rotated
-// across the XCDs by a mix of the block index, so that the splits and ranks
-// of one request spread over all XCDs even when a ragged batch concentrates
-// the work in a few units.
+// reads share that XCD's L2.  Each block of 8 consecutive work items is
+// rotated across the XCDs by a mix of the block index, so that the splits
+// and ranks of one request spread over all XCDs even when a ragged batch
+// concentrates the work in a few units.
 struct WgUnit {
   int rb;
   int64_t unit;
@@ -280,32 +292,28 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
 
   const WgUnit wu = wg_unit(blockIdx.x, p.n_row_blocks);
   const int rb = wu.rb;
-  const int64_t unit = wu.unit;
-  if (unit >= p.units_total) return;
-  const int split = (int)(unit % p.splits);
-  const int64_t rbu = unit / p.splits;
-  const int b = (int)(rbu % p.batch);
-  const int rl = (int)(rbu / p.batch);
-  const int64_t r = (int64_t)p.rank_begin + rl;
-  const int64_t c = p.c, P = p.page;
+  const int64_t item = wu.unit;
+  if (item >= *p.n_items) return;
+  const int32_t unit = p.item_unit[item];
+  const int b = unit % p.batch;
+  const int rl = unit / p.batch;
+  const int32_t ri = p.rank_begin + rl, Pi = p.page;
   const int row0 = rb * MB + rbq * 16;    // producer's first row
 
   const int32_t L = request_len(p, b, tid == 0);
   // all rank-local token indices fit in int32 (seq_len is int32)
-  const int32_t ri = (int32_t)r, Pi = (int32_t)P;
   auto visible = [&](int qi) -> int32_t { return visible_tokens(L, ri, p.c, p.q_len, qi, p.causal); };
-  const int32_t split_tok = (int32_t)p.split_tokens;
-  const int32_t j_begin = split * split_tok;
+  const int32_t j_begin = p.item_jb[item], j_stop = p.item_je[item];
   const int32_t n_wg = visible((rb * MB + MB - 1) / p.heads);
-  const int32_t j_end = min(n_wg, j_begin + split_tok);
-  const int32_t jlim = min(visible(row0 / p.heads), j_begin + split_tok);
+  const int32_t j_end = min(n_wg, j_stop);
+  const int32_t jlim = min(visible(row0 / p.heads), j_stop);
   // wave-uniform: every row of a 16-row block belongs to the same query index
   const int32_t jlim_s = __builtin_amdgcn_readfirstlane(jlim);
   const int n_st = j_end > j_begin ? (j_end - j_begin + STOK - 1) / STOK : 0;
-  // a split past the end of every row of the block writes nothing (the split
-  // combine reads only the splits that hold visible tokens of a row); split 0
-  // always writes, so that an empty shard still yields lse = -inf and o = 0
-  if (n_st == 0 && split > 0) return;
+  // a unit with one item writes o_part / lse_part directly; the items of a
+  // split unit write partials (lse in base 2) for the combine, also when this
+  // row block sees none of the item's tokens (lse = -inf, o = 0)
+  const bool single = p.unit_count[unit] == 1;
 
   const uint8_t* pool = p.pools + (int64_t)rl * p.pool_bytes;
   const float* spool = FP8 ? p.pool_scales + (int64_t)rl * p.cap : nullptr;
@@ -610,23 +618,26 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   }
 
   // ---- finalise
+  float* o_out = single ? p.o_part + (int64_t)unit * p.rows * kDv : p.ws_o + item * p.rows * kDv;
   if (producer) {
     const float l_tot = wave_sum_g(l_run);
     if (g == 0) {
       lds_l[rbq * 16 + j] = l_tot;
       const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
-      const int64_t orow = (((int64_t)rl * p.batch + b) * p.splits + split) * p.rows + row0 + j;
-      p.lse_out[orow] = p.out_base2 ? lse2 : lse2 * kLn2;
+      if (single)
+        p.lse_part[(int64_t)unit * p.rows + row0 + j] = p.out_base2 ? lse2 : lse2 * kLn2;
+      else
+        p.ws_lse[item * p.rows + row0 + j] = lse2;
     }
   }
   __syncthreads();
   if (!producer) {
-    const int64_t orow0 = (((int64_t)rl * p.batch + b) * p.splits + split) * p.rows + rb * MB + j;
+    const int64_t orow0 = rb * MB + j;
 #pragma unroll
     for (int q = 0; q < RGN; ++q) {
       const float lq = lds_l[q * 16 + j];
       const float inv = lq > 0.f ? 1.0f / lq : 0.f;
-      float* optr = p.o_out + (orow0 + q * 16) * kDv;
+      float* optr = o_out + (orow0 + q * 16) * kDv;
 #pragma unroll
       for (int d = 0; d < NDBC; ++d) {
         const int col = (cq * NDBC + d) * 16 + 4 * g;
@@ -636,30 +647,133 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   }
 }
 
-// Merge the KV splits of every (rank, request, row): ws [units][splits][rows] -> o_part, lse_part.
-// Only the splits that hold visible tokens of the row are read (at least
-// split 0, which the decode kernel always writes).
-__global__ void __launch_bounds__(256)
-split_combine_kernel(DecodeParams p, const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
-                     int64_t n_rows_total, int32_t out_base2, float* __restrict__ o_part,
-                     float* __restrict__ lse_part) {
-  const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+// ---- work plan --------------------------------------------------------------
+// One workgroup cuts every unit (rank, request) into work items of whole
+// 32-token stages.  The item length T (in stages) spreads the call's total
+// work W over about items_target items per row block, which gives every CU
+// a few items and keeps the largest at about half of a CU's share; T is
+// clamped to [t_min, t_max] (t_max: an item's page ids fit the workgroup's
+// LDS table).  A unit of s stages gets ceil(s / T) items of equal length.
+// Units with several items are listed first, so the longest work is
+// dispatched first.  Every unit gets at least one item (an empty one for a
+// rank that sees no token), so its outputs are always written.
+// Exclusive prefix sum over the 1024 threads of a workgroup (64-bit values):
+// wave scans with shuffles, then the 16 wave totals.  Returns the prefix and
+// sets total.
+__device__ __forceinline__ int64_t block_excl_scan(int64_t v, int64_t* wtot, int64_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wtot[wv] = x;
+  __syncthreads();
+  int64_t before = 0;
+  total = 0;
+  for (int i = 0; i < 16; ++i) {
+    const int64_t t = wtot[i];
+    if (i < wv) before += t;
+    total += t;
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
+__global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
+  __shared__ int64_t wtot[16];
+  const int tid = threadIdx.x;
+  auto unit_stages = [&](int32_t u) -> int32_t {
+    const int b = u % p.batch, rl = u / p.batch;
+    const int32_t L = request_len(p, b, false);
+    const int32_t n = visible_tokens(L, p.rank_begin + rl, p.c, p.q_len, p.q_len - 1, p.causal);
+    return (n + kStageTok - 1) / kStageTok;
+  };
+  int64_t w = 0;
+  for (int32_t u = tid; u < p.units; u += 1024) w += unit_stages(u);
+  int64_t W;
+  block_excl_scan(w, wtot, W);
+  int64_t T = (W + p.items_target - 1) / p.items_target;
+  T = T < p.t_min ? p.t_min : (T > p.t_max ? p.t_max : T);
+  auto plan_of = [&](int32_t st, int32_t& items, int32_t& len) {
+    if (st == 0) {
+      items = 1;
+      len = 0;
+      return;
+    }
+    items = (int32_t)((st + T - 1) / T);
+    len = (st + items - 1) / items;
+    items = (st + len - 1) / len;
+  };
+  // Units with several items are listed first, so the single-item units
+  // start after all of their items (a separate counting pass unless every
+  // unit fits one chunk of 1024).
+  int64_t multi_total = 0;
+  if (p.units > 1024) {
+    for (int32_t base = 0; base < p.units; base += 1024) {
+      const int32_t u = base + tid;
+      int32_t items = 0, len = 0;
+      if (u < p.units) plan_of(unit_stages(u), items, len);
+      int64_t tot;
+      block_excl_scan(items > 1 ? items : 0, wtot, tot);
+      multi_total += tot;
+    }
+  }
+  // item offsets: items of split units in the high 32 bits, single-item
+  // units in the low 32 bits; a second scan numbers the split units
+  int64_t carry = 0, carry_split = 0;
+  for (int32_t base = 0; base < p.units; base += 1024) {
+    const int32_t u = base + tid;
+    int32_t st = 0, items = 0, len = 0;
+    if (u < p.units) {
+      st = unit_stages(u);
+      plan_of(st, items, len);
+    }
+    int64_t tot, tot_split;
+    const int64_t off = carry + block_excl_scan(items > 1 ? ((int64_t)items << 32) : (int64_t)items, wtot, tot);
+    const int64_t nsplit = carry_split + block_excl_scan(items > 1 ? 1 : 0, wtot, tot_split);
+    if (p.units <= 1024) multi_total = tot >> 32;
+    if (u < p.units) {
+      const int32_t first = items > 1 ? (int32_t)(off >> 32) : (int32_t)(multi_total + (off & 0xffffffffLL));
+      p.unit_first[u] = first;
+      p.unit_count[u] = items;
+      for (int32_t k = 0; k < items; ++k) {
+        p.item_unit[first + k] = u;
+        p.item_jb[first + k] = k * len * kStageTok;
+        p.item_je[first + k] = min((k + 1) * len, st) * kStageTok;
+      }
+      if (items > 1) p.split_units[nsplit] = u;
+    }
+    carry += tot;
+    carry_split += tot_split;
+  }
+  if (tid == 0) {
+    p.n_items[0] = (int32_t)(multi_total + (carry & 0xffffffffLL));
+    p.n_items[1] = (int32_t)carry_split;
+  }
+}
+
+// Merge the items of every split unit, row by row: partials (lse in base 2)
+// -> o_part, lse_part in the requested base.  Units with one item were
+// written directly by the decode kernel.  Two rows per 256-thread block,
+// grid-stride over (split unit, row) pairs.
+__global__ void __launch_bounds__(256) split_combine_kernel(DecodeParams p) {
+  const int64_t n_pairs = (int64_t)p.n_items[1] * p.rows;
   const int col4 = threadIdx.x & 127;
-  if (row >= n_rows_total) return;
-  const int64_t unit = row / p.rows;
-  const int rr = (int)(row % p.rows);
-  const int b = (int)(unit % p.batch);
-  const int32_t rank = (int32_t)(p.rank_begin + unit / p.batch);
-  const int32_t L = request_len(p, b, false);
-  const int32_t vis = visible_tokens(L, rank, p.c, p.q_len, rr / p.heads, p.causal);
-  const int32_t nv = (int32_t)min<int64_t>(p.splits, max<int64_t>(1, (vis + p.split_tokens - 1) / p.split_tokens));
-  const float* o = ws_o + (unit * p.splits * p.rows + rr) * kDv;
-  const float* l = ws_lse + unit * p.splits * p.rows + rr;
-  f32x4 acc;
-  float lse2;
-  merge_row4(o, (int64_t)p.rows * kDv, l, p.rows, nv, true, col4, acc, lse2);
-  *reinterpret_cast<f32x4*>(o_part + row * kDv + 4 * col4) = acc;
-  if (col4 == 0) lse_part[row] = out_base2 ? lse2 : lse2 * kLn2;
+  for (int64_t pr = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7); pr < n_pairs; pr += (int64_t)gridDim.x * 2) {
+    const int32_t unit = p.split_units[pr / p.rows];
+    const int rr = (int)(pr % p.rows);
+    const int64_t first = p.unit_first[unit];
+    const int32_t cnt = p.unit_count[unit];
+    f32x4 acc;
+    float lse2;
+    merge_row4(p.ws_o + (first * p.rows + rr) * kDv, (int64_t)p.rows * kDv, p.ws_lse + first * p.rows + rr, p.rows,
+               cnt, true, col4, acc, lse2);
+    const int64_t row = (int64_t)unit * p.rows + rr;
+    *reinterpret_cast<f32x4*>(p.o_part + row * kDv + 4 * col4) = acc;
+    if (col4 == 0) p.lse_part[row] = p.out_base2 ? lse2 : lse2 * kLn2;
+  }
 }
 
 template <int RGN, bool FP8>
@@ -687,38 +801,31 @@ int device_cu_count() {
 
 DecodePlan plan_decode(int32_t c, int32_t page, bool fp8, int32_t rank_count, int32_t batch, int32_t q_len,
                        int32_t heads, int64_t max_seq_len) {
+  (void)fp8;
   DecodePlan pl{};
   pl.rows = q_len * heads;
   const int rg = pl.rows % 64 == 0 ? 4 : (pl.rows % 32 == 0 ? 2 : 1);
   pl.row_block = 16 * rg;
   pl.n_row_blocks = pl.rows / pl.row_block;
-  pl.stage_tokens = 32;
+  pl.stage_tokens = kStageTok;
+  pl.units = (int64_t)rank_count * batch;
   const int64_t n_r_max = (max_seq_len + c - 1) / c;
-  const int64_t stages_max = (n_r_max + pl.stage_tokens - 1) / pl.stage_tokens;
-  const int64_t units = (int64_t)rank_count * batch * pl.n_row_blocks;
-  const int64_t target = 2 * (int64_t)device_cu_count();
-  int64_t splits = units > 0 ? (target + units - 1) / units : 1;
-  // a split's page ids must fit the workgroup's LDS table of kMaxTab entries
-  int64_t max_split_tokens = fp8 ? 8192 : 4096;
-  const int64_t tab_tokens = (int64_t)(kMaxTab - 1) * page / pl.stage_tokens * pl.stage_tokens;
-  if (tab_tokens < max_split_tokens) max_split_tokens = tab_tokens;
-  splits = std::max<int64_t>(splits, (n_r_max + max_split_tokens - 1) / max_split_tokens);
-  // at least 4 stages per split, unless the page table bound asks for more splits
-  splits = std::min<int64_t>(splits, std::max<int64_t>((stages_max + 3) / 4,
-                                                       (n_r_max + max_split_tokens - 1) / max_split_tokens));
-  if (splits < 1) splits = 1;
-  int64_t per = stages_max > 0 ? (stages_max + splits - 1) / splits : 1;
-  if (per * pl.stage_tokens > max_split_tokens) per = max_split_tokens / pl.stage_tokens;
-  splits = stages_max > 0 ? (stages_max + per - 1) / per : 1;
-  pl.splits = (int32_t)splits;
-  pl.split_tokens = per * pl.stage_tokens;
-  pl.workspace_bytes =
-      splits > 1 ? (size_t)rank_count * batch * splits * pl.rows * (kDv + 1) * sizeof(float) : 0;
+  const int64_t stages_max = (n_r_max + kStageTok - 1) / kStageTok;
+  pl.t_max = (int32_t)std::max<int64_t>(1, (int64_t)(kMaxTab - 1) * page / kStageTok);
+  pl.t_min = std::min<int32_t>(8, pl.t_max);
+  pl.items_target = std::max<int32_t>(1, 2 * device_cu_count() / pl.n_row_blocks);
+  // the device plan makes at most units + max(items_target, units * ceil(stages_max / t_max)) items
+  pl.max_items = pl.units + std::max<int64_t>(pl.items_target, pl.units * ((stages_max + pl.t_max - 1) / pl.t_max));
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  pl.off_ws_lse = al((size_t)pl.max_items * pl.rows * kDv * sizeof(float));
+  pl.off_ints = pl.off_ws_lse + al((size_t)pl.max_items * pl.rows * sizeof(float));
+  pl.workspace_bytes = pl.off_ints + al((size_t)(2 + 3 * pl.max_items + 3 * pl.units) * sizeof(int32_t));
   return pl;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {
   if (a.batch == 0 || a.rank_count == 0) return hipSuccess;
+  if (pl.max_items > INT32_MAX / 2 || pl.units > INT32_MAX / 2) return hipErrorInvalidValue;
   DecodeParams prm{};
   const int row_bytes = a.fp8 ? kDqk : 2 * kDqk;
   prm.pools = (const uint8_t*)a.pools;
@@ -739,28 +846,33 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   prm.seq_len = a.seq_len;
   prm.max_seq_len = a.max_seq_len;
   prm.scale_log2 = a.sm_scale * kLog2e;
+  prm.out_base2 = a.base2 ? 1 : 0;
   prm.causal = a.causal ? 1 : 0;
-  prm.splits = pl.splits;
-  prm.split_tokens = pl.split_tokens;
+  prm.o_part = a.o_part;
+  prm.lse_part = a.lse_part;
   prm.n_row_blocks = pl.n_row_blocks;
-  prm.units_total = (int64_t)a.rank_count * a.batch * pl.splits;
+  prm.units = (int32_t)pl.units;
+  prm.max_items = (int32_t)pl.max_items;
+  prm.items_target = pl.items_target;
+  prm.t_min = pl.t_min;
+  prm.t_max = pl.t_max;
+  uint8_t* ws = (uint8_t*)a.workspace;
+  prm.ws_o = (float*)ws;
+  prm.ws_lse = (float*)(ws + pl.off_ws_lse);
+  int32_t* ints = (int32_t*)(ws + pl.off_ints);
+  prm.n_items = ints;
+  prm.item_unit = ints + 2;
+  prm.item_jb = prm.item_unit + pl.max_items;
+  prm.item_je = prm.item_jb + pl.max_items;
+  prm.unit_first = prm.item_je + pl.max_items;
+  prm.unit_count = prm.unit_first + pl.units;
+  prm.split_units = prm.unit_count + pl.units;
   prm.dev_status = a.dev_status;
-  float* ws_o = nullptr;
-  float* ws_lse = nullptr;
-  if (pl.splits > 1) {
-    ws_o = (float*)a.workspace;
-    ws_lse = ws_o + (size_t)a.rank_count * a.batch * pl.splits * pl.rows * kDv;
-    prm.o_out = ws_o;
-    prm.lse_out = ws_lse;
-    prm.out_base2 = 1;
-  } else {
-    prm.o_out = a.o_part;
-    prm.lse_out = a.lse_part;
-    prm.out_base2 = a.base2 ? 1 : 0;
-  }
-  const bool aligned = a.page % pl.stage_tokens == 0;
-  const int64_t grid = (prm.units_total + 7) / 8 * 8 * pl.n_row_blocks;
-  hipError_t e;
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, prm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool aligned = a.page % kStageTok == 0;
+  const int64_t grid = (pl.max_items + 7) / 8 * 8 * pl.n_row_blocks;
   const int rg = pl.row_block / 16;
   if (a.fp8)
     e = rg == 4 ? launch_pc<4, true>(prm, aligned, grid, stream)
@@ -768,10 +880,11 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   else
     e = rg == 4 ? launch_pc<4, false>(prm, aligned, grid, stream)
                 : (rg == 2 ? launch_pc<2, false>(prm, aligned, grid, stream) : launch_pc<1, false>(prm, aligned, grid, stream));
-  if (e != hipSuccess || pl.splits == 1) return e;
-  const int64_t n_rows_total = (int64_t)a.rank_count * a.batch * pl.rows;
-  hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)((n_rows_total + 1) / 2)), dim3(256), 0, stream, prm,
-                     ws_o, ws_lse, n_rows_total, a.base2 ? 1 : 0, a.o_part, a.lse_part);
+  if (e != hipSuccess || pl.max_items == pl.units) return e;
+  // at most (max_items - units) units are split; a grid-stride loop covers them
+  const int64_t pairs_max = std::min<int64_t>(pl.max_items - pl.units, pl.units) * pl.rows;
+  const int64_t cgrid = std::max<int64_t>(1, std::min<int64_t>((pairs_max + 1) / 2, 8 * device_cu_count()));
+  hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)cgrid), dim3(256), 0, stream, prm);
   return hipGetLastError();
 }
 

@@ -84,8 +84,9 @@ def test_host_argument_errors(lib):
     assert call(base=3) == -1
     assert call(maxl=2**31) == -2
     assert call(B=0) == 0
-    # a long context needs split workspace: none given
+    # every call needs its workspace (the work plan lives there): none given
     assert call(maxl=1 << 20, B=1) == -4
+    assert call() == -4
     # kv write / alloc
     assert lib.dcp_kv_write(ref, 16, None, 16, 4, 16, 16, 1, 4, 8, None, None, None, None) == -3
     assert lib.dcp_kv_write(ctypes.byref(_layout(kv=1)), 16, None, 16, 4, 16, 16, 1, 4, 16, None, None, None,
@@ -94,10 +95,16 @@ def test_host_argument_errors(lib):
     assert lib.dcp_alloc_virtual(ref, 16, 16, 16, 16, -1, 16, 4, None, None) == -1
 
 
-def test_workspace_size_matches_split_plan(lib):
+def test_workspace_size_covers_the_work_plan(lib):
     from kv_sharded_mla_amd import mla_decode_workspace_size
-    # short contexts need no split workspace; a 1M-token fp8 context does
-    assert mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 64, 1, 16, 32768) == 0
-    n = mla_decode_workspace_size(_layout(8, 64, 100, 1), 8, 4, 1, 64, 1 << 20)
-    assert n > 0 and n % (4 * 513) == 0
+    # every call plans its work items in the workspace, so the size is never 0 for valid
+    # arguments; it holds at least one partial (512 outputs + lse, fp32) per unit and row
+    units, rows = 8 * 64, 16
+    n = mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 64, 1, 16, 32768)
+    assert n >= units * rows * 513 * 4
+    # a longer context can only need more items
+    assert mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 64, 1, 16, 1 << 20) >= n
+    # small pages bound an item's length (its page ids fit the LDS table), so more items
+    assert mla_decode_workspace_size(_layout(8, 1, 100, 0), 8, 64, 1, 16, 1 << 20) > \
+        mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 64, 1, 16, 1 << 20)
     assert mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 4, 9, 64, 1000) == 0  # invalid -> 0

@@ -55,7 +55,11 @@ def test_no_compiler_vmcnt_waits_inside_decode_loop(asm):
     # loads per stage, or 9 for the 64-row bf16 kernel whose four consumer waves issue all
     # 36 loads of a stage, with at most two stages ahead).  A wait the compiler placed for
     # Q inside the loop would show up as a count such as 17, 16, ... 1.
+    # Waits before the first direct-to-LDS load (reading the work plan, Q and the page
+    # table) cannot interfere with the ring and are not checked.
     allowed = {0} | {k * n for n in (3, 4, 5, 6) for k in range(1, 7)} | {9, 18}
     for name, body in _kernels(asm).items():
-        waits = set(int(x) for x in re.findall(r"vmcnt\((\d+)\)", body))
+        first_dma = body.find("global_load_lds")
+        assert first_dma > 0, name
+        waits = set(int(x) for x in re.findall(r"vmcnt\((\d+)\)", body[first_dma:]))
         assert waits <= allowed, (name, sorted(waits))
