@@ -287,6 +287,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   const int w = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, j = lane & 15;
   const bool producer = w < RGN;
+  const bool consumer = w >= 4;           // waves RGN..3 (RGN < 4) only join the barriers
   const int rbq = w & 3;                  // producer: its row block
   const int cq = w & 3;                   // consumer: its column group
 
@@ -362,7 +363,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   // 1024), lane k the 16 bytes at 1024 i + 16 k, which hold chunk
   // (pos ^ swz(row)) of stage row `row` (pos = position inside the row)
   const int lw = w & 3;
-  const int ni = producer ? 0 : (lw < NBIG ? NI_MAX : NI_MAX - 1);
+  const int ni = consumer ? (lw < NBIG ? NI_MAX : NI_MAX - 1) : 0;
   int dma_row[NI_MAX];
   uint32_t dma_off[NI_MAX];
 #pragma unroll
@@ -592,7 +593,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   };
 
   // stages 0 .. NSTG-2 in flight; stage 0 resident before the first tile
-  if (!producer) {
+  if (consumer) {
     for (int s = 0; s < NSTG - 1 && s < n_st; ++s) issue(s, ALIGNED ? __builtin_amdgcn_readfirstlane(lds_pt[iss_pidx]) : 0);
     if (n_st > 0) wait_vmcnt_ahead<NI_MAX, NBIG, FP8, NSTG - 2>(lw, min(NSTG - 2, n_st - 1));
   }
@@ -603,18 +604,18 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     int32_t pg_next = 0;
     if (producer) {
       if (i < n_st) produce(i);
-    } else {
+    } else if (consumer) {
       // page id of the stage issued after this tile's barrier, read early
       if (ALIGNED && refill) pg_next = lds_pt[iss_pidx];
       if (i >= 1) consume(i - 1);
     }
     if (i == n_st) break;
     // stage i+1 must be resident for the next producer tile
-    if (!producer && i + 1 < n_st) wait_vmcnt_ahead<NI_MAX, NBIG, FP8, NSTG - 2>(lw, min(NSTG - 3, n_st - 2 - i));
+    if (consumer && i + 1 < n_st) wait_vmcnt_ahead<NI_MAX, NBIG, FP8, NSTG - 2>(lw, min(NSTG - 3, n_st - 2 - i));
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P^T and the rescale factors are in LDS
     wg_barrier();
     // the consumers are done with stage i-1: refill its slot
-    if (!producer && refill) issue(i + NSTG - 1, __builtin_amdgcn_readfirstlane(pg_next));
+    if (consumer && refill) issue(i + NSTG - 1, __builtin_amdgcn_readfirstlane(pg_next));
   }
 
   // ---- finalise
@@ -631,7 +632,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     }
   }
   __syncthreads();
-  if (!producer) {
+  if (consumer) {
     const int64_t orow0 = rb * MB + j;
 #pragma unroll
     for (int q = 0; q < RGN; ++q) {
