@@ -42,6 +42,8 @@ CASES = [
     ("fp8_h16_unaligned", W(index=66, H=16, c=2, P=16, fixed_len=333, kv_dtype="fp8"), None),
     ("fp8_verify", W(index=67, H=32, q_len=4, c=4, P=64, fixed_len=1500, kv_dtype="fp8", B=2), None),
     ("fp8_splits", W(index=68, H=64, c=1, P=64, fixed_len=40000, kv_dtype="fp8"), None),
+    ("fp8_one_to_four_stages", W(index=72, H=32, c=1, P=64, B=5, kv_dtype="fp8"), [1, 40, 70, 100, 128]),
+    ("fp8_empty_shards", W(index=73, H=64, c=8, P=16, fixed_len=5, kv_dtype="fp8"), None),
 ]
 
 
