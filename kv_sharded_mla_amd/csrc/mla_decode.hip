@@ -255,10 +255,10 @@ __device__ __forceinline__ int32_t visible_tokens(int32_t L, int32_t r, int32_t 
 // barriers.  One
 // workgroup barrier per tile hands P^T over and recycles the stage the
 // consumers finished; producer and consumer of a SIMD run different phases
-// and overlap.  Producers run at a raised wave priority, so their MFMAs go
-// first and the consumer's MFMAs fill the time of the producer's softmax;
-// the consumers also issue every direct-to-LDS load, which keeps the
-// producers' path from one barrier to the next free of load issue and waits.
+// and overlap (all waves at the same priority: a raised producer priority
+// measured 3-4% slower).  The consumers issue every direct-to-LDS load,
+// which keeps the producers' path from one barrier to the next free of load
+// issue and waits.
 template <int RGN, bool FP8, bool ALIGNED>
 __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams p) {
   static_assert(RGN == 1 || RGN == 2 || RGN == 4, "row blocks per workgroup");
@@ -598,7 +598,6 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     if (n_st > 0) wait_vmcnt_ahead<NI_MAX, NBIG, FP8, NSTG - 2>(lw, min(NSTG - 2, n_st - 1));
   }
   wg_barrier();
-  if (producer) __builtin_amdgcn_s_setprio(2);
   for (int i = 0; i <= n_st; ++i) {
     const bool refill = i + NSTG - 1 < n_st;
     int32_t pg_next = 0;

@@ -37,7 +37,7 @@ def test_m0_only_feeds_lds_dma(asm):
     assert uses, "expected the LDS-DMA m0 writes"
     for i in uses:
         ins = code[i].split(";")[0]
-        assert re.match(r"s_mov_b32 m0, s\d+$", ins), ins
+        assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", ins), ins
         assert code[i + 1].startswith("global_load_lds_dword"), code[i + 1]
 
 
