@@ -38,6 +38,9 @@ namespace dcp {
 
 namespace {
 
+#ifndef DCP_RB_LAG
+#define DCP_RB_LAG 1
+#endif
 constexpr int kWaves = 8;     // waves per workgroup: two per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr float kTau = 8.0f;
@@ -45,6 +48,12 @@ constexpr int kMaxTab = 512;  // page ids staged per workgroup
 constexpr int kStageTok = 32; // tokens per LDS stage
 // score fragments in token-block-major order (each accumulator then takes its
 // MFMAs back to back) or interleaved
+#ifndef DCP_FP8_SCALE_PREFETCH
+#define DCP_FP8_SCALE_PREFETCH 0
+#endif
+#ifndef DCP_FP8_TBMAJOR
+#define DCP_FP8_TBMAJOR 1
+#endif
 #ifndef DCP_PC_TBMAJOR
 #define DCP_PC_TBMAJOR 1
 #endif
@@ -119,6 +128,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // insertion does not treat the ring's later LDS reads as aliasing these
 // writes.  m0 carries the LDS address; nothing else in these kernels uses m0
 // (a host-side build check verifies this in the generated code).
+// Cache policy of the direct-to-LDS loads (NT): the non-temporal hint lifts
+// KV streaming from HBM from 6.14 to 7.26 TB/s, and is used when a work item
+// has one row block.  Items with several row blocks re-read their KV from L2
+// (one read per row block), which the hint defeats (15% slower).
+template <bool NT>
 __device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, const void* lds) {
   // gbase is wave-uniform; readfirstlane pins it (and the LDS address) to SGPRs
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
@@ -126,16 +140,26 @@ __device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, const
   const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)gbase);
   const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uintptr_t)gbase >> 32));
   const uint64_t gb = lo | (hi << 32);
-  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(gb)
-                   : "memory");
+  if (NT)
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(m0), "v"(voff), "s"(gb) : "memory");
+  else
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(gb) : "memory");
 }
+template <bool NT>
 __device__ __forceinline__ void dma16_abs(const uint8_t* gaddr, const void* lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gaddr) : "memory");
+  if (NT)
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(m0), "v"(gaddr) : "memory");
+  else
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gaddr) : "memory");
 }
+template <bool NT>
 __device__ __forceinline__ void dma4_abs(const float* gaddr, const void* lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(gaddr) : "memory");
+  if (NT)
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off nt" ::"s"(m0), "v"(gaddr) : "memory");
+  else
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(gaddr) : "memory");
 }
 
 // Workgroup barrier without the release fence of __syncthreads (which would
@@ -259,7 +283,7 @@ __device__ __forceinline__ int32_t visible_tokens(int32_t L, int32_t r, int32_t 
 // measured 3-4% slower).  The consumers issue every direct-to-LDS load,
 // which keeps the producers' path from one barrier to the next free of load
 // issue and waits.
-template <int RGN, bool FP8, bool ALIGNED>
+template <int RGN, bool FP8, bool ALIGNED, bool NT>
 __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams p) {
   static_assert(RGN == 1 || RGN == 2 || RGN == 4, "row blocks per workgroup");
   constexpr int MB = 16 * RGN;            // query rows per workgroup
@@ -304,13 +328,22 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   const int32_t L = request_len(p, b, tid == 0);
   // all rank-local token indices fit in int32 (seq_len is int32)
   auto visible = [&](int qi) -> int32_t { return visible_tokens(L, ri, p.c, p.q_len, qi, p.causal); };
-  const int32_t j_begin = p.item_jb[item], j_stop = p.item_je[item];
+  // item bounds and tile count are uniform: scalar registers
+  const int32_t j_begin = __builtin_amdgcn_readfirstlane(p.item_jb[item]);
+  const int32_t j_stop = __builtin_amdgcn_readfirstlane(p.item_je[item]);
   const int32_t n_wg = visible((rb * MB + MB - 1) / p.heads);
-  const int32_t j_end = min(n_wg, j_stop);
+  const int32_t j_end = __builtin_amdgcn_readfirstlane(min(n_wg, j_stop));
   const int32_t jlim = min(visible(row0 / p.heads), j_stop);
   // wave-uniform: every row of a 16-row block belongs to the same query index
   const int32_t jlim_s = __builtin_amdgcn_readfirstlane(jlim);
   const int n_st = j_end > j_begin ? (j_end - j_begin + STOK - 1) / STOK : 0;
+  // The row blocks of one item walk its tiles from different starting points
+  // (block rb starts DCP_RB_LAG * rb tiles ahead, wrapping around): the block
+  // that reaches a tile first takes the miss and the others find the rows in
+  // L2, instead of every block waiting on the same misses.  The order of the
+  // tiles does not change the result beyond rounding.
+  const int rot = n_st > 0 ? (rb * DCP_RB_LAG) % n_st : 0;
+  auto tile_of = [&](int s) { const int x = s + rot; return x < n_st ? x : x - n_st; };
   // a unit with one item writes o_part / lse_part directly; the items of a
   // split unit write partials (lse in base 2) for the combine, also when this
   // row block sees none of the item's tokens (lse = -inf, o = 0)
@@ -377,21 +410,21 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     const int32_t pidx = jj / Pi;
     return (int64_t)lds_pt[pidx - vp_first] * Pi + (jj - pidx * Pi);
   };
-  // next stage to issue: entry iss_pidx of the page table, token iss_rem of
-  // that page (tracked only when stages never straddle pages)
-  int32_t iss_pidx = 0, iss_rem = j_begin - vp_first * Pi;
+  // page-table entry of the page that holds stage s (whole-stage fast path:
+  // a stage never straddles pages)
+  auto stage_pidx = [&](int s) { return (j_begin + tile_of(s) * STOK) / Pi - vp_first; };
   // issue stage s; pg is the page id of the stage (whole-stage fast path)
   auto issue = [&](int s, int32_t pg) {
     uint8_t* dst = lds_kv + (s % NSTG) * SBYTES;
     float* dst_sc = lds_sc + (FP8 ? (s % NSTG) * STOK : 0);
-    const int32_t j0 = j_begin + s * STOK;
+    const int32_t j0 = j_begin + tile_of(s) * STOK;
     if (ALIGNED && j0 + STOK <= j_end) {
-      const int64_t slot0 = (int64_t)pg * Pi + iss_rem;
+      const int64_t slot0 = (int64_t)pg * Pi + (j0 - (j0 / Pi) * Pi);
       const uint8_t* base = pool + slot0 * ROWB;
 #pragma unroll
       for (int t = 0; t < NI_MAX; ++t)
-        if (t < ni) dma16(base, dma_off[t], dst + (lw + NLW * t) * 1024);
-      if (FP8 && lane < 8) dma4_abs(spool + slot0 + 8 * lw + lane, dst_sc + 8 * lw);
+        if (t < ni) dma16<NT>(base, dma_off[t], dst + (lw + NLW * t) * 1024);
+      if (FP8 && lane < 8) dma4_abs<NT>(spool + slot0 + 8 * lw + lane, dst_sc + 8 * lw);
     } else {
       // last stage of a split (rows past j_end repeat the last valid row) or
       // pages that a stage can straddle
@@ -399,19 +432,12 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
       for (int t = 0; t < NI_MAX; ++t)
         if (t < ni) {
           const int32_t jj = min(j0 + dma_row[t], j_end - 1);
-          dma16_abs(pool + slot_of(jj) * ROWB + (dma_off[t] - dma_row[t] * ROWB), dst + (lw + NLW * t) * 1024);
+          dma16_abs<NT>(pool + slot_of(jj) * ROWB + (dma_off[t] - dma_row[t] * ROWB), dst + (lw + NLW * t) * 1024);
         }
       if (FP8) {
         const int32_t jj = min(j0 + 8 * lw + (lane & 7), j_end - 1);
         const float* src = spool + slot_of(jj);
-        if (lane < 8) dma4_abs(src, dst_sc + 8 * lw);
-      }
-    }
-    if (ALIGNED) {
-      iss_rem += STOK;
-      if (iss_rem >= Pi) {
-        iss_rem -= Pi;
-        ++iss_pidx;
+        if (lane < 8) dma4_abs<NT>(src, dst_sc + 8 * lw);
       }
     }
   };
@@ -449,21 +475,32 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   auto produce = [&](int t) {
     const uint8_t* kv = lds_kv + (t % NSTG) * SBYTES;
     const float* sc = lds_sc + (FP8 ? (t % NSTG) * STOK : 0);
-    const int32_t jt = j_begin + t * STOK;
+    const int32_t jt = j_begin + tile_of(t) * STOK;
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // e4m3 token scales of this lane's 8 tokens, read before the score
+    // MFMAs so that their LDS latency is hidden
+    float tsc[8];
+    if (FP8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tsc[e] = sc[(e >> 2) * 16 + 4 * g + (e & 3)];
+      if (DCP_FP8_SCALE_PREFETCH) __asm__ volatile("" ::: "memory");
+    }
     // K fragments f = 2u + tb (k unit u, token block tb), kept PD loads ahead
     // of the MFMA that uses them; the schedule below pins that interleave.
     if (FP8) {
       constexpr int NF = 2 * KU, PD = 6;
       i32x4 kf[NF];
-      // fragment f = KU*tb + u (token-block major, as for bf16)
-      auto kload = [&](int f) { return *reinterpret_cast<const i32x4*>(kv + koff[f / KU][0] + 64 * (f % KU)); };
+      // fragment f: k unit u of token block tb, token-block major (each
+      // accumulator's MFMAs back to back) or alternating between the blocks
+      auto ftb = [](int f) { return DCP_FP8_TBMAJOR ? f / KU : f & 1; };
+      auto fu = [](int f) { return DCP_FP8_TBMAJOR ? f % KU : f >> 1; };
+      auto kload = [&](int f) { return *reinterpret_cast<const i32x4*>(kv + koff[ftb(f)][0] + 64 * fu(f)); };
 #pragma unroll
       for (int f = 0; f < PD; ++f) kf[f] = kload(f);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         if (f + PD < NF) kf[f + PD] = kload(f + PD);
-        const int u = f % KU, tb = f / KU;
+        const int u = fu(f), tb = ftb(f);
         sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{kf[f][0], kf[f][1]}), qf(2 * u), sacc[tb], 0, 0, 0);
         sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{kf[f][2], kf[f][3]}), qf(2 * u + 1), sacc[tb], 0, 0, 0);
       }
@@ -504,14 +541,11 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     // is detected with a ballot and only then is the row maximum formed
     // across the lanes of the row.  exp2 is the hardware instruction: a
     // probability below 2^-126 flushes to zero, far below what bf16 P keeps.
-    float y[8], tsc[8];
+    float y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       y[e] = sacc[e >> 2][e & 3];
-      if (FP8) {
-        tsc[e] = sc[(e >> 2) * 16 + 4 * g + (e & 3)];
-        y[e] *= tsc[e];
-      }
+      if (FP8) y[e] *= tsc[e];
       y[e] *= p.scale_log2;
     }
     if (jt + STOK > jlim_s) {  // the tile reaches past this row block's last visible token
@@ -594,7 +628,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
 
   // stages 0 .. NSTG-2 in flight; stage 0 resident before the first tile
   if (consumer) {
-    for (int s = 0; s < NSTG - 1 && s < n_st; ++s) issue(s, ALIGNED ? __builtin_amdgcn_readfirstlane(lds_pt[iss_pidx]) : 0);
+    for (int s = 0; s < NSTG - 1 && s < n_st; ++s) issue(s, ALIGNED ? __builtin_amdgcn_readfirstlane(lds_pt[stage_pidx(s)]) : 0);
     if (n_st > 0) wait_vmcnt_ahead<NI_MAX, NBIG, FP8, NSTG - 2>(lw, min(NSTG - 2, n_st - 1));
   }
   wg_barrier();
@@ -605,7 +639,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
       if (i < n_st) produce(i);
     } else if (consumer) {
       // page id of the stage issued after this tile's barrier, read early
-      if (ALIGNED && refill) pg_next = lds_pt[iss_pidx];
+      if (ALIGNED && refill) pg_next = lds_pt[stage_pidx(i + NSTG - 1)];
       if (i >= 1) consume(i - 1);
     }
     if (i == n_st) break;
@@ -778,10 +812,12 @@ __global__ void __launch_bounds__(256) split_combine_kernel(DecodeParams p) {
 
 template <int RGN, bool FP8>
 hipError_t launch_pc(const DecodeParams& prm, bool aligned, int64_t grid, hipStream_t stream) {
-  if (aligned)
-    hipLaunchKernelGGL((mla_decode_pc_kernel<RGN, FP8, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, prm);
-  else
-    hipLaunchKernelGGL((mla_decode_pc_kernel<RGN, FP8, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, prm);
+  const dim3 g((unsigned)grid), b(kThreads);
+  const bool nt = prm.n_row_blocks == 1;
+  if (aligned && nt) hipLaunchKernelGGL((mla_decode_pc_kernel<RGN, FP8, true, true>), g, b, 0, stream, prm);
+  else if (aligned) hipLaunchKernelGGL((mla_decode_pc_kernel<RGN, FP8, true, false>), g, b, 0, stream, prm);
+  else if (nt) hipLaunchKernelGGL((mla_decode_pc_kernel<RGN, FP8, false, true>), g, b, 0, stream, prm);
+  else hipLaunchKernelGGL((mla_decode_pc_kernel<RGN, FP8, false, false>), g, b, 0, stream, prm);
   return hipGetLastError();
 }
 

@@ -43,8 +43,8 @@ def test_m0_only_feeds_lds_dma(asm):
 
 def test_decode_kernels_do_not_spill(asm):
     ks = _kernels(asm)
-    # 1, 2 or 4 row blocks x bf16/e4m3 x page-aligned or not
-    assert len(ks) == 12 and all("pc_kernel" in k for k in ks)
+    # 1, 2 or 4 row blocks x bf16/e4m3 x page-aligned or not x non-temporal loads or not
+    assert len(ks) == 24 and all("pc_kernel" in k for k in ks)
     for name, body in ks.items():
         assert "scratch_" not in body, name
 
@@ -63,3 +63,15 @@ def test_no_compiler_vmcnt_waits_inside_decode_loop(asm):
         assert first_dma > 0, name
         waits = set(int(x) for x in re.findall(r"vmcnt\((\d+)\)", body[first_dma:]))
         assert waits <= allowed, (name, sorted(waits))
+
+
+def test_non_temporal_loads_only_in_single_row_block_kernels(asm):
+    # template argument 4 (NT) of mla_decode_pc_kernel: Lb1E at the end of the mangled name
+    for name, body in _kernels(asm).items():
+        loads = re.findall(r"global_load_lds_dword\S*[^\n]*", body)
+        assert loads, name
+        nt = [l for l in loads if re.search(r"\bnt\b", l)]
+        if name.endswith("Lb1EEEvNS0_12DecodeParamsE"):
+            assert len(nt) == len(loads), name
+        else:
+            assert not nt, name
