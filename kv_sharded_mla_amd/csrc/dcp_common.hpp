@@ -49,16 +49,27 @@ __device__ __forceinline__ bool merge_row4(const float* __restrict__ o, int64_t 
     lse_out = -INFINITY;
     return false;
   }
-  // work in base 2: w_r = 2^(lse2_r - m2)
+  // work in base 2: w_r = 2^(lse2_r - m2).  The partials are loaded 8 at a
+  // time before they are combined (in order r = 0, 1, ...), so the loads
+  // overlap instead of each waiting for the previous one.
   const float to2 = in_base2 ? 1.0f : kLog2e;
   float tot = 0.f;
-  for (int r = 0; r < nparts; ++r) {
-    float l = lse[r * lse_stride];
-    if (l == -INFINITY) continue;
-    float w = exp2f((l - m) * to2);
-    tot += w;
-    f32x4 v = *reinterpret_cast<const f32x4*>(o + r * o_stride + 4 * col4);
-    acc += w * v;
+  for (int r0 = 0; r0 < nparts; r0 += 8) {
+    float l[8];
+    f32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (r0 + k < nparts) {
+        l[k] = lse[(r0 + k) * lse_stride];
+        v[k] = *reinterpret_cast<const f32x4*>(o + (r0 + k) * o_stride + 4 * col4);
+      }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (r0 + k < nparts && l[k] != -INFINITY) {
+        const float w = exp2f((l[k] - m) * to2);
+        tot += w;
+        acc += w * v[k];
+      }
   }
   float inv = 1.0f / tot;
   acc *= inv;

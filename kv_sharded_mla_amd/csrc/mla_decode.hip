@@ -788,8 +788,10 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     const int32_t n = visible_tokens(L, p.rank_begin + rl, p.c, p.q_len, p.q_len - 1, p.causal);
     return (n + kStageTok - 1) / kStageTok;
   };
-  int64_t w = 0;
-  for (int32_t u = tid; u < p.units; u += 1024) w += unit_stages(u);
+  // the first chunk's stage counts stay in a register (one read of seq_len)
+  const int32_t st0 = tid < p.units ? unit_stages(tid) : 0;
+  int64_t w = st0;
+  for (int32_t u = tid + 1024; u < p.units; u += 1024) w += unit_stages(u);
   int64_t W;
   block_excl_scan(w, wtot, W);
   int64_t T = (W + p.items_target - 1) / p.items_target;
@@ -812,7 +814,7 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     for (int32_t base = 0; base < p.units; base += 1024) {
       const int32_t u = base + tid;
       int32_t items = 0, len = 0;
-      if (u < p.units) plan_of(unit_stages(u), items, len);
+      if (u < p.units) plan_of(base == 0 ? st0 : unit_stages(u), items, len);
       int64_t tot;
       block_excl_scan(items > 1 ? items : 0, wtot, tot);
       multi_total += tot;
@@ -825,7 +827,7 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     const int32_t u = base + tid;
     int32_t st = 0, items = 0, len = 0;
     if (u < p.units) {
-      st = unit_stages(u);
+      st = base == 0 ? st0 : unit_stages(u);
       plan_of(st, items, len);
     }
     int64_t tot, tot_split;
@@ -983,7 +985,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   if (e != hipSuccess || pl.max_items == pl.units) return e;
   // at most (max_items - units) units are split; a grid-stride loop covers them
   const int64_t pairs_max = std::min<int64_t>(pl.max_items - pl.units, pl.units) * pl.rows;
-  const int64_t cgrid = std::max<int64_t>(1, std::min<int64_t>((pairs_max + 1) / 2, 8 * device_cu_count()));
+  const int64_t cgrid = std::max<int64_t>(1, std::min<int64_t>((pairs_max + 1) / 2, 2 * device_cu_count()));
   hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)cgrid), dim3(256), 0, stream, prm);
   return hipGetLastError();
 }
