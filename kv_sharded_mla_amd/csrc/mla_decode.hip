@@ -194,8 +194,6 @@ __device__ __forceinline__ void wait_vmcnt_ahead(int w, int ahead) {
   else wait_stages<NI - 1 + (FP8 ? 1 : 0), MAXA>(ahead);
 }
 
-typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
-
 __device__ __forceinline__ bf16x8 cvt_fp8x8(i32x2 v) {
   bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[0], 1.0f, false);
   bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[0], 1.0f, true);
@@ -375,65 +373,12 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   // its O^T accumulators (8 blocks x 4 row blocks) in R[0..31].
   constexpr int NR = NDBC * RGN > 18 ? NDBC * RGN : 18;
   f32x4 R[NR];
-  // e4m3 KV: the 512 latent dims of Q are held as two e4m3 parts per row,
-  // q = 2^e_row * (hi + lo / 16) up to rounding of lo, so the score MFMAs
-  // take the K codes as they are; R[0..7] hold hi and R[8..15] lo (lane (g, j):
-  // dims 128 kb + 32 g .. +31 of row j, kb = 0..3, 32 bytes per kb), R[16..17]
-  // the rope dims in bf16.  sc_hi / sc_lo: the E8M0 scales 2^e_row and
-  // 2^(e_row - 4) that the MFMAs apply to hi and lo.
-  int sc_hi = 127, sc_lo = 123;
   if (producer) {
     const uint16_t* qrow = p.q + ((int64_t)b * p.rows + row0 + j) * kDqk;
-    if (FP8) {
-      // rope: the k-step pairs of the bf16 path (16 e4m3 codes per K load)
 #pragma unroll
-      for (int kk = 16; kk < 18; ++kk)
-        R[kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + 64 * (kk >> 1) + 16 * g + 8 * (kk & 1)));
-      // latent: row maximum over the 4 lanes of the row, then the two parts
-      bf16x8 qv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) qv[i] = *reinterpret_cast<const bf16x8*>(qrow + 128 * (i >> 2) + 32 * g + 8 * (i & 3));
-      float mx = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf((float)qv[i][e]));
-      mx = wave_max_g(mx);
-      // 2^-e maps the row maximum below 128, so hi <= 128 and |lo| <= 256 fit e4m3
-      int ex = 0;
-      if (mx > 0.f) (void)frexpf(mx, &ex);
-      const int e_row = min(max(ex - 7, -120), 120);
-      sc_hi = 127 + e_row;
-      sc_lo = 123 + e_row;
-      const float down = ldexpf(1.f, -e_row);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        int hi[8], lo[8];
-#pragma unroll
-        for (int dw = 0; dw < 8; ++dw) {
-          float v[4], rsd[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = (float)qv[4 * kb + (dw >> 1)][4 * (dw & 1) + t] * down;
-          int h = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-          h = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], h, true);
-          rsd[0] = (v[0] - __builtin_amdgcn_cvt_f32_fp8(h, 0)) * 16.f;
-          rsd[1] = (v[1] - __builtin_amdgcn_cvt_f32_fp8(h, 1)) * 16.f;
-          rsd[2] = (v[2] - __builtin_amdgcn_cvt_f32_fp8(h, 2)) * 16.f;
-          rsd[3] = (v[3] - __builtin_amdgcn_cvt_f32_fp8(h, 3)) * 16.f;
-          int l = __builtin_amdgcn_cvt_pk_fp8_f32(rsd[0], rsd[1], 0, false);
-          l = __builtin_amdgcn_cvt_pk_fp8_f32(rsd[2], rsd[3], l, true);
-          hi[dw] = h;
-          lo[dw] = l;
-        }
-        R[2 * kb] = __builtin_bit_cast(f32x4, i32x4{hi[0], hi[1], hi[2], hi[3]});
-        R[2 * kb + 1] = __builtin_bit_cast(f32x4, i32x4{hi[4], hi[5], hi[6], hi[7]});
-        R[8 + 2 * kb] = __builtin_bit_cast(f32x4, i32x4{lo[0], lo[1], lo[2], lo[3]});
-        R[8 + 2 * kb + 1] = __builtin_bit_cast(f32x4, i32x4{lo[4], lo[5], lo[6], lo[7]});
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk)
-        R[kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * g));
+    for (int kk = 0; kk < 18; ++kk) {
+      const int col = FP8 ? 64 * (kk >> 1) + 16 * g + 8 * (kk & 1) : 32 * kk + 8 * g;
+      R[kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + col));
     }
   } else {
 #pragma unroll
@@ -498,16 +443,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   };
 
   // producer K offsets (both token blocks) and consumer V^T offsets
-  int koff[2][2], voff[2][4], koff8[2][2];
+  int koff[2][2], voff[2][4];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
     const int row = 16 * tb + j;
     if (FP8) {
       koff[tb][0] = row * ROWB + 16 * (g ^ swz<true>(row));
       koff[tb][1] = koff[tb][0];
-      // latent chunk 8kb + 2g + h of the row sits at 8kb + ((2g + h) ^ swz)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) koff8[tb][h] = row * ROWB + 16 * ((2 * g + h) ^ swz<true>(row));
     } else {
 #pragma unroll
       for (int par = 0; par < 2; ++par) koff[tb][par] = row * ROWB + 16 * ((4 * par + g) ^ swz<false>(row));
@@ -546,35 +488,29 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     // K fragments f = 2u + tb (k unit u, token block tb), kept PD loads ahead
     // of the MFMA that uses them; the schedule below pins that interleave.
     if (FP8) {
-      // latent: per token block and kb, 32 K codes per lane (chunks 8kb+2g and
-      // 8kb+2g+1 of row 16tb+j) times the hi and lo parts of Q; the two token
-      // blocks alternate so that consecutive MFMAs are independent.  rope:
-      // chunk 32+g of the row, converted to bf16, two bf16 MFMAs per block.
-      i32x4 kl[2][4][2], kr[2];
+      constexpr int NF = 2 * KU, PD = 6;
+      i32x4 kf[NF];
+      // fragment f: k unit u of token block tb, token-block major (each
+      // accumulator's MFMAs back to back) or alternating between the blocks
+      auto ftb = [](int f) { return DCP_FP8_TBMAJOR ? f / KU : f & 1; };
+      auto fu = [](int f) { return DCP_FP8_TBMAJOR ? f % KU : f >> 1; };
+      auto kload = [&](int f) { return *reinterpret_cast<const i32x4*>(kv + koff[ftb(f)][0] + 64 * fu(f)); };
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int f = 0; f < PD; ++f) kf[f] = kload(f);
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) kl[tb][kb][h] = *reinterpret_cast<const i32x4*>(kv + koff8[tb][h] + 128 * kb);
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) kr[tb] = *reinterpret_cast<const i32x4*>(kv + koff[tb][0] + 64 * 8);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const i32x8 qh = __builtin_bit_cast(i32x8, __builtin_shufflevector(__builtin_bit_cast(i32x4, R[2 * kb]), __builtin_bit_cast(i32x4, R[2 * kb + 1]), 0, 1, 2, 3, 4, 5, 6, 7));
-        const i32x8 ql = __builtin_bit_cast(i32x8, __builtin_shufflevector(__builtin_bit_cast(i32x4, R[8 + 2 * kb]), __builtin_bit_cast(i32x4, R[8 + 2 * kb + 1]), 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(kl[tb][kb][0], kl[tb][kb][1], 0, 1, 2, 3, 4, 5, 6, 7));
-          sacc[tb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qh, sacc[tb], 0, 0, 0, 127, 0, sc_hi);
-          sacc[tb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, ql, sacc[tb], 0, 0, 0, 127, 0, sc_lo);
-        }
+      for (int f = 0; f < NF; ++f) {
+        if (f + PD < NF) kf[f + PD] = kload(f + PD);
+        const int u = fu(f), tb = ftb(f);
+        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{kf[f][0], kf[f][1]}), qf(2 * u), sacc[tb], 0, 0, 0);
+        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{kf[f][2], kf[f][3]}), qf(2 * u + 1), sacc[tb], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{kr[tb][0], kr[tb][1]}), qf(16), sacc[tb], 0, 0, 0);
-        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt_fp8x8(i32x2{kr[tb][2], kr[tb][3]}), qf(17), sacc[tb], 0, 0, 0);
+      for (int f = 0; f < NF - PD; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * PD, 0);
     } else {
       // fragment f = KU*tb + u: each accumulator takes its 18 MFMAs back to back
       constexpr int NF = 2 * KU, PD = 8;

@@ -89,3 +89,35 @@ def test_decode_pages_beyond_4gib(kv, H):
     bt = case.group.block_table.cpu().numpy()
     assert bt[bt >= 0].min() * 64 * row > (1 << 30)
     check_case(case)
+
+
+def _scale_q_rows(case, exps):
+    """Multiply each query row r by 2**exps[r % len(exps)] (exact in bf16)."""
+    qb = case.q_bits
+    f = (qb.astype(np.uint32) << 16).view(np.float32).reshape(qb.shape)
+    rows = f.reshape(f.shape[0], -1, f.shape[-1])
+    for r in range(rows.shape[1]):
+        rows[:, r, :] *= np.float32(2.0 ** exps[r % len(exps)])
+    case.q_bits = (rows.reshape(qb.shape).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.isfinite(rows).all()
+    case.q = __import__("torch").from_numpy(case.q_bits.view(np.int16)).to("cuda")
+
+
+@pytest.mark.parametrize("k", [-40, 40])
+def test_fp8_query_magnitudes_far_from_one(k):
+    # e4m3 scores take q as two e4m3 parts under a per-row power-of-two scale:
+    # a q 2^k times larger, with a softmax scale 2^-k times smaller, must give
+    # the same attention
+    w = W(index=74, H=64, c=4, P=64, fixed_len=700, B=2, kv_dtype="fp8", sm_scale=C.SM_SCALE * 2.0 ** (-k))
+    case = Case(w)
+    _scale_q_rows(case, [k])
+    log(f"q scaled by 2^{k}")
+    check_case(case)
+
+
+def test_fp8_query_rows_of_different_magnitudes():
+    # rows 2^-4 .. 2^4 apart in one 16-row block: each row gets its own scale
+    w = W(index=75, H=64, c=2, P=64, fixed_len=500, B=2, kv_dtype="fp8")
+    case = Case(w)
+    _scale_q_rows(case, [-4, -3, -2, -1, 0, 1, 2, 3, 4])
+    check_case(case)
