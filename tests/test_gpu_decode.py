@@ -103,21 +103,39 @@ def _scale_q_rows(case, exps):
     case.q = __import__("torch").from_numpy(case.q_bits.view(np.int16)).to("cuda")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("k", [-40, 40])
-def test_fp8_query_magnitudes_far_from_one(k):
-    # e4m3 scores take q as two e4m3 parts under a per-row power-of-two scale:
-    # a q 2^k times larger, with a softmax scale 2^-k times smaller, must give
-    # the same attention
-    w = W(index=74, H=64, c=4, P=64, fixed_len=700, B=2, kv_dtype="fp8", sm_scale=C.SM_SCALE * 2.0 ** (-k))
+def test_query_magnitudes_far_from_one(kv, k):
+    # a q 2^k times larger, with a softmax scale 2^-k times smaller, is the
+    # same attention; scores and the running maximum must not lose it
+    w = W(index=74, H=64, c=4, P=64, fixed_len=700, B=2, kv_dtype=kv, sm_scale=C.SM_SCALE * 2.0 ** (-k))
     case = Case(w)
     _scale_q_rows(case, [k])
-    log(f"q scaled by 2^{k}")
+    log(f"{kv}: q scaled by 2^{k}")
     check_case(case)
 
 
-def test_fp8_query_rows_of_different_magnitudes():
-    # rows 2^-4 .. 2^4 apart in one 16-row block: each row gets its own scale
-    w = W(index=75, H=64, c=2, P=64, fixed_len=500, B=2, kv_dtype="fp8")
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_query_rows_of_different_magnitudes(kv):
+    # rows 2^-4 .. 2^4 apart in one 16-row block (sharp and flat softmax side
+    # by side).  The score arithmetic is held to the stated lse tolerance.  A
+    # sharp row makes o close to a single V row (|o| up to ~4 here), and then
+    # the bf16 P of the PV product and the bf16 output each round by up to
+    # 2^-9 |o|, which alone can exceed the absolute 1e-2: o is held to
+    # max(stated tolerance, 2^-7 max|o|) instead.
+    from parity import TOL
+    w = W(index=75, H=64, c=2, P=64, fixed_len=500, B=2, kv_dtype=kv)
     case = Case(w)
     _scale_q_rows(case, [-4, -3, -2, -1, 0, 1, 2, 3, 4])
-    check_case(case)
+    o_part, lse_part, o, lse = case.run()
+    to, tl = TOL[kv]
+    for b in range(w.B):
+        ro, rl, rop, rlp = case.oracle(b)
+        for name, got_o, got_l, ref_o, ref_l in (("merged", o[b], lse[b], ro, rl), ("partials", o_part[:, b], lse_part[:, b], rop, rlp)):
+            fin = ~np.isneginf(ref_l)
+            assert np.array_equal(fin, ~np.isneginf(got_l)), name
+            dl = float(np.abs(got_l[fin] - ref_l[fin]).max())
+            do = float(np.abs(got_o - ref_o).max())
+            bound = max(to, 2.0 ** -7 * float(np.abs(ref_o).max()))
+            log(f"{kv} b={b} {name}: max|do|={do:.3e} (bound {bound:.3e}) max|dlse|={dl:.3e} (tol {tl})")
+            assert dl <= tl and do <= bound, (name, do, bound, dl)
