@@ -92,13 +92,15 @@ def to_base(lse_e: np.ndarray, base: str) -> np.ndarray:
 
 
 def decode_attention(q_bits: np.ndarray, kv, L: int, sm_scale: float, causal: bool = True,
-                     base: str = "e", c: int = 1, r: Optional[int] = None, chunk: int = CHUNK):
+                     base: str = "e", c: int = 1, r: Optional[int] = None, chunk: int = CHUNK,
+                     I: int = 1):
     """Attention of one request's query rows over its KV (or rank r's share of it).
 
     q_bits  uint16 [q_len][H][576] bf16 payloads
     kv      (data, scale): logical rows in position order, data uint16 [L][576]
             (bf16) or uint8 [L][576] (e4m3) with float32 scale [L]
-    r       None: all positions; else only positions p with p mod c == r
+    r       None: all positions; else only the positions rank r owns, p with
+            floor(p / I) mod c == r (interleave I; I = 1: p mod c == r)
     Returns o float64 [q_len][H][512] and lse float64 [q_len][H] in ``base``.
     """
     q_len, H, _ = q_bits.shape
@@ -111,10 +113,13 @@ def decode_attention(q_bits: np.ndarray, kv, L: int, sm_scale: float, causal: bo
         def fetch(a, z):
             return decode_rows(data[a:z], None if scale is None else scale[a:z]), np.arange(a, z)
     else:
-        n = (L - r + c - 1) // c if L > r else 0
+        # rank r's j-th position is floor(j / I) I c + r I + j mod I
+        full = L // (I * c)
+        n = full * I + min(max(L - full * I * c - r * I, 0), I)
 
         def fetch(a, z):
-            pos = r + c * np.arange(a, z)
+            j = np.arange(a, z)
+            pos = (j // I) * I * c + r * I + j % I
             return decode_rows(data[pos], None if scale is None else scale[pos]), pos
     o, lse = attend(q, fetch, n, lim, sm_scale, chunk)
     return o.reshape(q_len, H, D_V), to_base(lse, base).reshape(q_len, H)
@@ -143,7 +148,7 @@ def merge(o_parts: np.ndarray, lse_parts: np.ndarray, base: str = "e"):
     return o, to_base(lse_ln, base)
 
 
-def rank_partials(q_bits, kv, L, sm_scale, c, causal=True, base="e"):
+def rank_partials(q_bits, kv, L, sm_scale, c, causal=True, base="e", I=1):
     """(o_r, lse_r) for every rank r of a c-way striped group: [c][q_len][H][512], [c][q_len][H]."""
-    outs = [decode_attention(q_bits, kv, L, sm_scale, causal, base, c=c, r=r) for r in range(c)]
+    outs = [decode_attention(q_bits, kv, L, sm_scale, causal, base, c=c, r=r, I=I) for r in range(c)]
     return np.stack([o for o, _ in outs]), np.stack([l for _, l in outs])

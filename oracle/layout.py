@@ -21,7 +21,16 @@ checks compare against):
   (request, logical page) order; a call that cannot be satisfied takes no
   page at all (all-or-nothing).
 * New rows of request b occupy the last n_b positions before seq_len[b].
-* Interleave size is one token: owner(p) depends on p mod c only.
+* Interleave size I (the vLLM study page "vLLM Decode Context Parallelism",
+  section on operation, configuration example: a KV interleave size, one
+  token by default, larger chunks for less sorting work at some imbalance):
+  consecutive chunks of I positions go to the ranks in turn, owner(p) =
+  floor(p / I) mod c, and I divides P so that every virtual page still gives
+  each rank exactly P positions.  In virtual-slot terms owner(v) =
+  floor(v / I) mod c and physical(v) = floor(v / (I c)) I + v mod I, which
+  are the pages' v mod c and floor(v / c) at I = 1.  Rank r's j-th position
+  is then p = floor(j / I) I c + r I + j mod I, and its page is floor(j / P),
+  so the shared block table is still the rank-local page table.
 
 Status codes mirror the library's documented device status values; they are
 restated here rather than imported.
@@ -39,12 +48,12 @@ TABLE_OVERFLOW = 3
 BAD_PAGE = 4
 
 
-def owner(v: int, c: int) -> int:
-    return v % c
+def owner(v: int, c: int, I: int = 1) -> int:
+    return (v // I) % c
 
 
-def physical(v: int, c: int) -> int:
-    return v // c
+def physical(v: int, c: int, I: int = 1) -> int:
+    return (v // (I * c)) * I + v % I
 
 
 def virtual_page_size(P: int, c: int) -> int:
@@ -67,10 +76,10 @@ def virtual_slot(bt_row: Sequence[int], p: int, P: int, c: int) -> int:
     return int(bt_row[p // vp]) * vp + p % vp
 
 
-def slot_of(bt_row: Sequence[int], p: int, P: int, c: int) -> Tuple[int, int]:
+def slot_of(bt_row: Sequence[int], p: int, P: int, c: int, I: int = 1) -> Tuple[int, int]:
     """(owner rank, physical slot in that rank's pool) of logical position p."""
     v = virtual_slot(bt_row, p, P, c)
-    return owner(v, c), physical(v, c)
+    return owner(v, c, I), physical(v, c, I)
 
 
 def alloc_virtual(free_stack: np.ndarray, free_top: int, old_len: Sequence[int],
@@ -101,7 +110,7 @@ def alloc_virtual(free_stack: np.ndarray, free_top: int, old_len: Sequence[int],
 
 
 def write_slots(block_table: np.ndarray, seq_len: Sequence[int], cu_new: Sequence[int],
-                P: int, c: int, num_pages: int):
+                P: int, c: int, num_pages: int, I: int = 1):
     """Destination of every new row: (status, owner[N], phys[N]); -1 where skipped."""
     B = len(seq_len)
     N = int(cu_new[B])
@@ -125,13 +134,13 @@ def write_slots(block_table: np.ndarray, seq_len: Sequence[int], cu_new: Sequenc
             if page < 0 or page >= num_pages:
                 status = max(status, BAD_PAGE)
                 continue
-            r, s = slot_of(block_table[b], p, P, c)
+            r, s = slot_of(block_table[b], p, P, c, I)
             own[row], phys[row] = r, s
     return status, own, phys
 
 
 def pool_image(pools: np.ndarray, block_table: np.ndarray, seq_len, cu_new, rows: np.ndarray,
-               P: int, c: int, scales: np.ndarray = None, pool_scales: np.ndarray = None):
+               P: int, c: int, scales: np.ndarray = None, pool_scales: np.ndarray = None, I: int = 1):
     """Expected pool bytes after scattering ``rows`` into a copy of ``pools``.
 
     ``pools`` is [c][num_pages*P][row elements] in the stored dtype.
@@ -139,7 +148,7 @@ def pool_image(pools: np.ndarray, block_table: np.ndarray, seq_len, cu_new, rows
     out = np.array(pools, copy=True)
     outs = None if pool_scales is None else np.array(pool_scales, copy=True)
     num_pages = out.shape[1] // P
-    status, own, phys = write_slots(block_table, seq_len, cu_new, P, c, num_pages)
+    status, own, phys = write_slots(block_table, seq_len, cu_new, P, c, num_pages, I)
     for n in range(len(own)):
         if own[n] >= 0:
             out[own[n], phys[n]] = rows[n]
@@ -148,15 +157,16 @@ def pool_image(pools: np.ndarray, block_table: np.ndarray, seq_len, cu_new, rows
     return status, own, phys, out, outs
 
 
-def owned_positions(length: int, c: int, r: int) -> np.ndarray:
+def owned_positions(length: int, c: int, r: int, I: int = 1) -> np.ndarray:
     """Logical positions of a request of ``length`` tokens that rank r owns, ascending."""
-    return np.array([p for p in range(length) if owner(p, c) == r], dtype=np.int64)
+    return np.array([p for p in range(length) if owner(p, c, I) == r], dtype=np.int64)
 
 
-def owned_count(length: int, c: int, r: int) -> int:
-    return sum(1 for p in range(length) if p % c == r)
+def owned_count(length: int, c: int, r: int, I: int = 1) -> int:
+    return sum(1 for p in range(length) if (p // I) % c == r)
 
 
-def rank_local_slots(block_table_row: Sequence[int], length: int, P: int, c: int, r: int) -> List[int]:
+def rank_local_slots(block_table_row: Sequence[int], length: int, P: int, c: int, r: int,
+                     I: int = 1) -> List[int]:
     """Physical slots, in rank r's pool, of the positions r owns, in position order."""
-    return [slot_of(block_table_row, int(p), P, c)[1] for p in owned_positions(length, c, r)]
+    return [slot_of(block_table_row, int(p), P, c, I)[1] for p in owned_positions(length, c, r, I)]

@@ -248,3 +248,33 @@ def test_planted_merge_mistakes_fail_partition_pin(kind):
     o = (wn[..., None] * o_p).sum(0)
     lse = ln.max(0) + np.log(tot)
     assert np.abs(o - o_full).max() > 1e-9 or np.abs(lse - lse_full).max() > 1e-9
+
+
+@pytest.mark.parametrize("I,causal,q_len", [(2, True, 1), (4, True, 4), (16, True, 4), (3, False, 2)])
+def test_interleaved_partials_merge_to_full_attention(I, causal, q_len):
+    # the ranks' shares under interleave I partition the context: the exact merge
+    # of their partials is the full attention (and the causal limits of the
+    # verify rows hold per rank)
+    rng = np.random.default_rng(11 + I)
+    L, c = 97, 4
+    q, kv = _case(rng, q_len, 2, L)
+    o_full, l_full = A.decode_attention(q, kv, L, SCALE, causal, "e")
+    op, lp = A.rank_partials(q, kv, L, SCALE, c, causal, "e", I=I)
+    o, l = A.merge(op, lp, "e")
+    assert np.abs(o - o_full).max() < 1e-12 and np.abs(l - l_full).max() < 1e-12
+
+
+def test_interleaved_rank_share_is_the_dealt_positions():
+    # rank r's partial with interleave I equals full attention over exactly the
+    # positions dealt to r in chunks of I (built without the closed form)
+    rng = np.random.default_rng(5)
+    L, c, I = 50, 3, 4
+    q, (kv, _) = _case(rng, 1, 2, L)
+    dealt = [[] for _ in range(c)]
+    for p in range(L):
+        dealt[(p // I) % c].append(p)
+    for r in range(c):
+        pos = np.array(dealt[r])
+        o_r, l_r = A.decode_attention(q, (kv, None), L, SCALE, False, "e", c=c, r=r, I=I)
+        o_s, l_s = A.decode_attention(q, (kv[pos], None), len(pos), SCALE, False, "e")
+        assert np.abs(o_r - o_s).max() < 1e-12 and np.abs(l_r - l_s).max() < 1e-12

@@ -154,3 +154,67 @@ def test_pool_image_sentinel_untouched():
             if (r, s) not in written:
                 assert (out[r, s] == 0xEE).all()      # a partial last page leaks nothing
     assert len(written) == 5
+
+
+# ---- interleave size I > 1 -------------------------------------------------
+# Pinned against a constructive model written without the closed forms: each
+# virtual page of P*c positions is dealt to the ranks in chunks of I
+# consecutive positions, rank after rank, and every rank appends what it is
+# dealt to its own physical page in arrival order.
+
+def _dealt(P, c, I, n_pages):
+    """position -> (rank, physical slot) for pages 0..n_pages-1 with identity page ids."""
+    out = {}
+    for g in range(n_pages):
+        fill = [0] * c
+        pos = g * P * c
+        rank = 0
+        while pos < (g + 1) * P * c:
+            for _ in range(I):
+                out[pos] = (rank, g * P + fill[rank])
+                fill[rank] += 1
+                pos += 1
+            rank = (rank + 1) % c
+    return out
+
+
+@pytest.mark.parametrize("c,P,I", [(2, 4, 2), (3, 6, 3), (4, 8, 2), (4, 16, 16), (8, 16, 4), (1, 8, 4), (3, 4, 1)])
+def test_interleaved_slots_match_dealing(c, P, I):
+    n_pages = 5
+    want = _dealt(P, c, I, n_pages)
+    bt = list(range(n_pages))
+    for p, (r, s) in want.items():
+        assert layout.slot_of(bt, p, P, c, I) == (r, s), (p, r, s)
+    # each (rank, slot) of a virtual page is used exactly once
+    assert len(set(want.values())) == len(want)
+
+
+@pytest.mark.parametrize("c,I", [(2, 2), (3, 4), (4, 16), (8, 8), (5, 3)])
+def test_interleaved_ownership_and_balance(c, I):
+    for L in range(0, 3 * I * c + 5):
+        counts = [layout.owned_count(L, c, r, I) for r in range(c)]
+        assert sum(counts) == L
+        assert max(counts) - min(counts) <= I
+        for r in range(c):
+            pos = layout.owned_positions(L, c, r, I)
+            assert len(pos) == counts[r]
+            # rank r's j-th position in closed form
+            j = np.arange(len(pos))
+            assert np.array_equal(pos, (j // I) * I * c + r * I + j % I)
+
+
+@pytest.mark.parametrize("c,P,I", [(2, 4, 2), (4, 16, 4), (3, 12, 6)])
+def test_interleaved_rank_local_page_table_is_the_block_table(c, P, I):
+    rng = np.random.default_rng(7)
+    bt = rng.permutation(40)[:8]
+    for L in (1, P * c - 1, P * c, 3 * P * c + 5, 8 * P * c):
+        for r in range(c):
+            n = layout.owned_count(L, c, r, I)
+            want = [int(bt[j // P]) * P + j % P for j in range(n)]
+            assert layout.rank_local_slots(bt, L, P, c, r, I) == want
+
+
+def test_interleave_one_is_the_token_cycle():
+    for v in range(200):
+        for c in (1, 2, 3, 8):
+            assert layout.owner(v, c, 1) == v % c and layout.physical(v, c, 1) == v // c
