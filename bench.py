@@ -70,7 +70,7 @@ def cpu_baseline(w, lens, budget_s: float):
         L = int(lens[b])
         kv = gen.kv_rows(w, b, L)           # stored-format bytes (generation not timed)
         t0 = time.perf_counter()
-        op, lp = OA.rank_partials(q_bits[b], kv, L, w.sm_scale, w.c, w.causal, w.lse_base)
+        op, lp = OA.rank_partials(q_bits[b], kv, L, w.sm_scale, w.c, w.causal, w.lse_base, I=w.interleave)
         OA.merge(op, lp, w.lse_base)
         t_total += time.perf_counter() - t0
         done_bytes += L * accounting.kv_bytes_per_token(w)
@@ -92,6 +92,8 @@ def main():
     ap.add_argument("--copies", type=int, default=2, help="pool copies used in rotation")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--interleave", type=int, default=None,
+                    help="KV interleave size I (a divisor of the page size; the workload's own by default)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (HBM counter calibration)")
     ap.add_argument("--decode-only", type=int, default=0,
@@ -110,6 +112,8 @@ def main():
     from workloads import accounting, configs, gen
 
     w = configs.BY_NAME[args.config]
+    if args.interleave is not None:
+        w = configs.scaled(w, interleave=args.interleave, name=w.name)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     K.load_library()
     dev = torch.device("cuda:0")
@@ -139,7 +143,8 @@ def main():
     ctx_sc = torch.from_numpy(scale[ctx_idx]).to(dev) if scale is not None else None
     del data, scale, row_u8
     for k in range(args.copies):
-        g = DcpGroup(w.c, w.P, num_pages, kv_kind, w.B, stride, free_stack=stack, device="cuda:0")
+        g = DcpGroup(w.c, w.P, num_pages, kv_kind, w.B, stride, free_stack=stack, device="cuda:0",
+                     interleave=w.interleave)
         g.append([int(x) for x in ctx], ctx_rows, ctx_sc)
         groups.append(g)
     del ctx_rows, ctx_sc
@@ -255,7 +260,7 @@ def main():
         "data": "synthetic (seeded N(0,1) q and latent KV" + (", e4m3 + fp32 per-token scale" if w.kv_dtype == "fp8"
                                                               else ", bf16") + ")",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "q_len": w.q_len, "dcp": w.c, "page": w.P,
-                   "kv": w.kv_dtype, "context_tokens": int(lens.sum()), "max_len": max_len,
+                   "interleave": w.interleave, "kv": w.kv_dtype, "context_tokens": int(lens.sum()), "max_len": max_len,
                    "lse_base": w.lse_base, "emulated_ranks_on_one_gpu": w.c},
         "us_per_layer_step": round(ms_per_step * 1e3, 2),
         "tflops": round(tflops, 2),

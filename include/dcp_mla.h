@@ -81,10 +81,19 @@ enum { DCP_LSE_BASE_E = 0, DCP_LSE_BASE_2 = 1 };
 
 /* Geometry of one DCP group's paged latent cache (host struct). */
 typedef struct dcp_layout {
-  int32_t c;         /* DCP group size, >= 1                                  */
-  int32_t page;      /* physical page size P in tokens, >= 1                  */
-  int32_t num_pages; /* physical pages per owner pool; capacity C = num_pages*page */
-  int32_t kv_dtype;  /* DCP_KV_BF16 or DCP_KV_FP8_E4M3                        */
+  int32_t c;          /* DCP group size, >= 1                                  */
+  int32_t page;       /* physical page size P in tokens, >= 1                  */
+  int32_t num_pages;  /* physical pages per owner pool; capacity C = num_pages*page */
+  int32_t kv_dtype;   /* DCP_KV_BF16 or DCP_KV_FP8_E4M3                        */
+  int32_t interleave; /* KV interleave size I in tokens (0 or 1: one token);
+                         I must divide page.  vLLM study page "vLLM Decode
+                         Context Parallelism", operation guide, configuration
+                         example: consecutive chunks of I positions go to the
+                         ranks in turn, owner(p) = floor(p / I) mod c.  Every
+                         virtual page of P*c positions still gives each rank P
+                         of them, so the block table stays the rank-local page
+                         table.  A negative I, or one that does not divide
+                         page: DCP_ERR_INVALID_ARG                            */
 } dcp_layout;
 
 /* Bytes of one rank's pool (num_pages * page * row bytes). */
@@ -125,7 +134,8 @@ int dcp_alloc_virtual(const dcp_layout* layout, const int32_t* free_stack, int32
  * rank sees the same request-to-token map, keeps the positions it owns and
  * compacts them into its physical pool.  Position p of request b has virtual
  * slot v = block_table[b][p / (P*c)] * P*c + p mod (P*c); its owner is
- * v mod c and its physical slot there is v / c.
+ * v mod c and its physical slot there is v / c (interleave I: owner
+ * floor(v / I) mod c, physical slot floor(v / (I*c)) * I + v mod I).
  *
  * Request b appends rows cu_new[b] .. cu_new[b+1]-1 (n_b rows) at positions
  * seq_len[b]-n_b .. seq_len[b]-1 (seq_len is the length after the append).
@@ -169,9 +179,10 @@ size_t mla_decode_workspace_size(const dcp_layout* layout, int32_t rank_count, i
  * kernel is given the group size, the rank and the global KV length so that
  * causality is judged on global positions.
  *
- * Rank r's j-th owned token is global position p = j*c + r and sits at
- * physical slot block_table[b][j / P] * P + j mod P of pool r (the shared
- * block table is the rank-local page table).  For query row (b, i, h), with
+ * Rank r's j-th owned token is global position p = j*c + r (interleave I:
+ * p = floor(j / I)*I*c + r*I + j mod I) and sits at physical slot
+ * block_table[b][j / P] * P + j mod P of pool r (the shared block table is
+ * the rank-local page table).  For query row (b, i, h), with
  * i < q_len and global length L = seq_len[b], the visible positions are
  * p <= L - q_len + i when causal, all p < L otherwise.  Scores are
  * sm_scale * <q, K_p> over the 576 columns, (times the row's scale for e4m3);

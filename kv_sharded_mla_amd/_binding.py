@@ -40,10 +40,11 @@ class DcpError(RuntimeError):
 
 class Layout(ctypes.Structure):
     _fields_ = [("c", ctypes.c_int32), ("page", ctypes.c_int32),
-                ("num_pages", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+                ("num_pages", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("interleave", ctypes.c_int32)]
 
     def __repr__(self):
-        return f"Layout(c={self.c}, page={self.page}, num_pages={self.num_pages}, kv_dtype={self.kv_dtype})"
+        return (f"Layout(c={self.c}, page={self.page}, num_pages={self.num_pages}, kv_dtype={self.kv_dtype}, "
+                f"interleave={self.interleave})")
 
 
 _lib = None
@@ -112,8 +113,8 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel=None) -> int:
     return int(t.data_ptr())
 
 
-def make_layout(c: int, page: int, num_pages: int, kv_dtype: int = KV_BF16) -> Layout:
-    return Layout(int(c), int(page), int(num_pages), int(kv_dtype))
+def make_layout(c: int, page: int, num_pages: int, kv_dtype: int = KV_BF16, interleave: int = 1) -> Layout:
+    return Layout(int(c), int(page), int(num_pages), int(kv_dtype), int(interleave))
 
 
 def dcp_pool_bytes(layout: Layout) -> int:

@@ -9,9 +9,14 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// interleave 0 means one token, as 1 does
+int32_t interleave_of(const dcp_layout* l) { return l->interleave < 1 ? 1 : l->interleave; }
+
 int check_layout(const dcp_layout* l) {
   if (!l) return DCP_ERR_INVALID_ARG;
   if (l->c < 1 || l->page < 1 || l->num_pages < 0) return DCP_ERR_INVALID_ARG;
+  // every virtual page must give each rank exactly P positions
+  if (l->interleave < 0 || l->page % interleave_of(l) != 0) return DCP_ERR_INVALID_ARG;
   if (l->kv_dtype != DCP_KV_BF16 && l->kv_dtype != DCP_KV_FP8_E4M3) return DCP_ERR_INVALID_ARG;
   // every slot index of the group must fit in int64 with room to spare
   if ((int64_t)l->num_pages * l->page > ((int64_t)1 << 40)) return DCP_ERR_UNSUPPORTED;
@@ -58,7 +63,7 @@ int dcp_kv_write(const dcp_layout* layout, void* pools, float* pool_scales, cons
   if (!aligned(pools, 16) || !aligned(rows, 16)) return DCP_ERR_ALIGNMENT;
   if (fp8 && (!aligned(pool_scales, 4) || !aligned(row_scales, 4))) return DCP_ERR_ALIGNMENT;
   if (slot_out && !aligned(slot_out, 8)) return DCP_ERR_ALIGNMENT;
-  return hip_status(dcp::launch_kv_write(layout->c, layout->page, layout->num_pages, fp8, pools, pool_scales,
+  return hip_status(dcp::launch_kv_write(layout->c, interleave_of(layout), layout->page, layout->num_pages, fp8, pools, pool_scales,
                                          block_table, bt_stride, seq_len, cu_new, batch, n_rows, rows, row_scales,
                                          slot_out, dev_status, stream));
 }
@@ -68,8 +73,9 @@ size_t mla_decode_workspace_size(const dcp_layout* layout, int32_t rank_count, i
   if (check_layout(layout) != DCP_OK || rank_count < 1 || batch < 0 || q_len < 1 || q_len > DCP_MAX_Q_LEN ||
       heads < 16 || heads % 16 != 0 || max_seq_len < 0)
     return 0;
-  dcp::DecodePlan pl = dcp::plan_decode(layout->c, layout->page, layout->kv_dtype == DCP_KV_FP8_E4M3, rank_count, batch, q_len,
-                                        heads, max_seq_len);
+  dcp::DecodePlan pl = dcp::plan_decode(layout->c, interleave_of(layout), layout->page,
+                                        layout->kv_dtype == DCP_KV_FP8_E4M3, rank_count, batch, q_len, heads,
+                                        max_seq_len);
   return pl.workspace_bytes;
 }
 
@@ -93,13 +99,15 @@ int mla_decode_partial(const dcp_layout* layout, const void* pools, const float*
   if (!aligned(pools, 16) || !aligned(q, 16) || !aligned(o_part, 16) || !aligned(lse_part, 4))
     return DCP_ERR_ALIGNMENT;
   if (fp8 && !aligned(pool_scales, 4)) return DCP_ERR_ALIGNMENT;
-  dcp::DecodePlan pl = dcp::plan_decode(layout->c, layout->page, fp8, rank_count, batch, q_len, heads, max_seq_len);
+  dcp::DecodePlan pl = dcp::plan_decode(layout->c, interleave_of(layout), layout->page, fp8, rank_count, batch, q_len,
+                                        heads, max_seq_len);
   if (pl.workspace_bytes > 0) {
     if (!workspace || workspace_bytes < pl.workspace_bytes) return DCP_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return DCP_ERR_ALIGNMENT;
   }
   dcp::DecodeArgs a{};
   a.c = layout->c;
+  a.interleave = interleave_of(layout);
   a.page = layout->page;
   a.num_pages = layout->num_pages;
   a.fp8 = fp8;

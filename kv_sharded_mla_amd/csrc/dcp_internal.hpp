@@ -12,7 +12,7 @@ hipError_t launch_alloc_virtual(int32_t c, int32_t page, const int32_t* free_sta
                                 int32_t* block_table, int32_t bt_stride, int32_t* dev_status,
                                 hipStream_t stream);
 
-hipError_t launch_kv_write(int32_t c, int32_t page, int32_t num_pages, bool fp8, void* pools,
+hipError_t launch_kv_write(int32_t c, int32_t interleave, int32_t page, int32_t num_pages, bool fp8, void* pools,
                            float* pool_scales, const int32_t* block_table, int32_t bt_stride,
                            const int32_t* seq_len, const int32_t* cu_new, int32_t batch,
                            int64_t n_rows, const void* rows, const float* row_scales,
@@ -38,11 +38,11 @@ struct DecodePlan {
   size_t workspace_bytes;
 };
 
-DecodePlan plan_decode(int32_t c, int32_t page, bool fp8, int32_t rank_count, int32_t batch, int32_t q_len,
-                       int32_t heads, int64_t max_seq_len);
+DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, int32_t rank_count, int32_t batch,
+                       int32_t q_len, int32_t heads, int64_t max_seq_len);
 
 struct DecodeArgs {
-  int32_t c, page, num_pages;
+  int32_t c, interleave, page, num_pages;
   bool fp8;
   const void* pools;
   const float* pool_scales;

@@ -4,7 +4,11 @@
 // virtual capacity C*c, virtual page P*c, owner(v) = v mod c,
 // physical(v) = floor(v / c).  A virtual page id is a page index valid in every
 // owner pool, so virtual page g covers physical slots [g*P, (g+1)*P) on each
-// rank.  Both kernels are integer/byte work and bit-exact by construction.
+// rank.  With a KV interleave size I (vLLM study page "vLLM Decode Context
+// Parallelism", operation guide) runs of I slots go to the owners in turn:
+// owner(v) = floor(v / I) mod c, physical(v) = floor(v / (I c)) I + v mod I,
+// and since I divides P the page mapping above is unchanged.  Both kernels are
+// integer/byte work and bit-exact by construction.
 #include "dcp_common.hpp"
 #include "dcp_internal.hpp"
 
@@ -83,7 +87,7 @@ alloc_virtual_kernel(int32_t c, int32_t page, const int32_t* __restrict__ free_s
 // its position from seq_len, its slot from the shared block table.
 template <bool FP8>
 __global__ void __launch_bounds__(256)
-kv_write_kernel(int32_t c, int32_t page, int32_t num_pages, uint8_t* __restrict__ pools,
+kv_write_kernel(int32_t c, int32_t il, int32_t page, int32_t num_pages, uint8_t* __restrict__ pools,
                 float* __restrict__ pool_scales, const int32_t* __restrict__ block_table,
                 int32_t bt_stride, const int32_t* __restrict__ seq_len,
                 const int32_t* __restrict__ cu_new, int32_t batch, int64_t n_rows,
@@ -117,9 +121,10 @@ kv_write_kernel(int32_t c, int32_t page, int32_t num_pages, uint8_t* __restrict_
       if (pg < 0 || pg >= num_pages) {
         code = DCP_DEV_BAD_PAGE;
       } else {
+        // chunks of il positions go to the ranks in turn (il divides the page)
         int64_t v = (int64_t)pg * vpage + p % vpage;
-        owner = v % c;
-        phys = v / c;
+        owner = (v / il) % c;
+        phys = (v / ((int64_t)il * c)) * il + v % il;
       }
     }
     if (code != DCP_DEV_OK) {
@@ -150,7 +155,7 @@ hipError_t launch_alloc_virtual(int32_t c, int32_t page, const int32_t* free_sta
   return hipGetLastError();
 }
 
-hipError_t launch_kv_write(int32_t c, int32_t page, int32_t num_pages, bool fp8, void* pools,
+hipError_t launch_kv_write(int32_t c, int32_t interleave, int32_t page, int32_t num_pages, bool fp8, void* pools,
                            float* pool_scales, const int32_t* block_table, int32_t bt_stride,
                            const int32_t* seq_len, const int32_t* cu_new, int32_t batch,
                            int64_t n_rows, const void* rows, const float* row_scales,
@@ -159,11 +164,11 @@ hipError_t launch_kv_write(int32_t c, int32_t page, int32_t num_pages, bool fp8,
   int64_t blocks = (n_rows + 3) / 4;
   if (blocks > 16384) blocks = 16384;
   if (fp8)
-    hipLaunchKernelGGL(kv_write_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, c, page, num_pages,
+    hipLaunchKernelGGL(kv_write_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, c, interleave, page, num_pages,
                        (uint8_t*)pools, pool_scales, block_table, bt_stride, seq_len, cu_new, batch, n_rows,
                        (const uint8_t*)rows, row_scales, slot_out, dev_status);
   else
-    hipLaunchKernelGGL(kv_write_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, c, page, num_pages,
+    hipLaunchKernelGGL(kv_write_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, c, interleave, page, num_pages,
                        (uint8_t*)pools, pool_scales, block_table, bt_stride, seq_len, cu_new, batch, n_rows,
                        (const uint8_t*)rows, row_scales, slot_out, dev_status);
   return hipGetLastError();

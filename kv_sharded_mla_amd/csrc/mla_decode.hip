@@ -63,7 +63,7 @@ struct DecodeParams {
   const float* pool_scales;
   int64_t pool_bytes;
   int64_t cap;  // tokens per pool
-  int32_t c, page, num_pages, rank_begin;
+  int32_t c, interleave, page, num_pages, rank_begin;
   const uint16_t* q;
   int32_t batch, q_len, heads, rows;
   const int32_t* block_table;
@@ -256,16 +256,25 @@ __device__ __forceinline__ int32_t request_len(const DecodeParams& p, int b, boo
   return L;
 }
 
-// Rank-local tokens of rank r that query index qi sees: rank r owns positions
-// j*c + r (j < n_r); a causal query qi of a q_len-token verification step sits
-// at global position L - q_len + qi and sees positions up to it.
-__device__ __forceinline__ int32_t visible_tokens(int32_t L, int32_t r, int32_t c, int32_t q_len, int32_t qi,
-                                                  int32_t causal) {
-  const int32_t n_r = L > r ? (L - r + c - 1) / c : 0;
+// Positions below x that rank r owns when runs of il consecutive positions go
+// to the ranks in turn: il per full cycle of il*c positions, plus the part of
+// r's run in the last, partial cycle.
+__device__ __forceinline__ int32_t owned_below(int32_t x, int32_t r, int32_t c, int32_t il) {
+  if (x <= 0) return 0;
+  const int64_t cyc = (int64_t)il * c;
+  const int64_t full = x / cyc;
+  const int64_t rest = x - full * cyc - (int64_t)r * il;
+  return (int32_t)(full * il + (rest < 0 ? 0 : (rest > il ? il : rest)));
+}
+
+// Rank-local tokens of rank r that query row qi sees: every owned position
+// below L, or (causal) at most L - q_len + qi, where a verification step's
+// query qi sits.  Rank r's positions rise with its local index, so the
+// visible ones are a prefix of its shard.
+__device__ __forceinline__ int32_t visible_tokens(int32_t L, int32_t r, int32_t c, int32_t il, int32_t q_len,
+                                                  int32_t qi, int32_t causal) {
   const int32_t lim = causal ? L - q_len + qi : L - 1;
-  if (lim < r) return 0;
-  const int32_t n = (lim - r) / c + 1;
-  return n < n_r ? n : n_r;
+  return owned_below((lim + 1 < L ? lim + 1 : L), r, c, il);
 }
 
 // Decode kernel: a workgroup of 8 waves owns RGN row blocks of 16 query rows
@@ -327,7 +336,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
 
   const int32_t L = request_len(p, b, tid == 0);
   // all rank-local token indices fit in int32 (seq_len is int32)
-  auto visible = [&](int qi) -> int32_t { return visible_tokens(L, ri, p.c, p.q_len, qi, p.causal); };
+  auto visible = [&](int qi) -> int32_t { return visible_tokens(L, ri, p.c, p.interleave, p.q_len, qi, p.causal); };
   // item bounds and tile count are uniform: scalar registers
   const int32_t j_begin = __builtin_amdgcn_readfirstlane(p.item_jb[item]);
   const int32_t j_stop = __builtin_amdgcn_readfirstlane(p.item_je[item]);
@@ -721,7 +730,7 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   auto unit_stages = [&](int32_t u) -> int32_t {
     const int b = u % p.batch, rl = u / p.batch;
     const int32_t L = request_len(p, b, false);
-    const int32_t n = visible_tokens(L, p.rank_begin + rl, p.c, p.q_len, p.q_len - 1, p.causal);
+    const int32_t n = visible_tokens(L, p.rank_begin + rl, p.c, p.interleave, p.q_len, p.q_len - 1, p.causal);
     return (n + kStageTok - 1) / kStageTok;
   };
   // the first chunk's stage counts stay in a register (one read of seq_len)
@@ -837,8 +846,8 @@ int device_cu_count() {
   return cached[dev];
 }
 
-DecodePlan plan_decode(int32_t c, int32_t page, bool fp8, int32_t rank_count, int32_t batch, int32_t q_len,
-                       int32_t heads, int64_t max_seq_len) {
+DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, int32_t rank_count, int32_t batch,
+                       int32_t q_len, int32_t heads, int64_t max_seq_len) {
   (void)fp8;
   DecodePlan pl{};
   pl.rows = q_len * heads;
@@ -847,7 +856,9 @@ DecodePlan plan_decode(int32_t c, int32_t page, bool fp8, int32_t rank_count, in
   pl.n_row_blocks = pl.rows / pl.row_block;
   pl.stage_tokens = kStageTok;
   pl.units = (int64_t)rank_count * batch;
-  const int64_t n_r_max = (max_seq_len + c - 1) / c;
+  // a rank owns at most ceil(L / (I c)) chunks of I positions of a request of L
+  const int64_t cyc = (int64_t)interleave * c;
+  const int64_t n_r_max = (max_seq_len + cyc - 1) / cyc * interleave;
   const int64_t stages_max = (n_r_max + kStageTok - 1) / kStageTok;
   pl.t_max = (int32_t)std::max<int64_t>(1, (int64_t)(kMaxTab - 1) * page / kStageTok);
   pl.t_min = std::min<int32_t>(8, pl.t_max);
@@ -871,6 +882,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   prm.cap = (int64_t)a.num_pages * a.page;
   prm.pool_bytes = prm.cap * row_bytes;
   prm.c = a.c;
+  prm.interleave = a.interleave;
   prm.page = a.page;
   prm.num_pages = a.num_pages;
   prm.rank_begin = a.rank_begin;

@@ -18,8 +18,10 @@ from . import _binding as B
 
 class DcpGroup:
     def __init__(self, c: int, page: int, num_pages: int, kv_dtype: int, batch: int, bt_stride: int,
-                 free_stack: Optional[np.ndarray] = None, device: str = "cuda", sentinel: Optional[int] = None):
-        self.layout = B.make_layout(c, page, num_pages, kv_dtype)
+                 free_stack: Optional[np.ndarray] = None, device: str = "cuda", sentinel: Optional[int] = None,
+                 interleave: int = 1):
+        self.layout = B.make_layout(c, page, num_pages, kv_dtype, interleave)
+        self.interleave = interleave
         self.c, self.page, self.num_pages, self.batch = c, page, num_pages, batch
         self.fp8 = kv_dtype == B.KV_FP8_E4M3
         self.device = torch.device(device)

@@ -41,7 +41,8 @@ class Case:
         self.bt_stride = max(1, max((int(L) + vp - 1) // vp for L in self.lens))
         fs = gen.free_stack(w, self.num_pages) if seed_free_stack else None
         self.group = DcpGroup(w.c, w.P, self.num_pages, KV_FP8_E4M3 if w.kv_dtype == "fp8" else KV_BF16,
-                              w.B, self.bt_stride, free_stack=fs, sentinel=sentinel)
+                              w.B, self.bt_stride, free_stack=fs, sentinel=sentinel,
+                              interleave=w.interleave)
         data, scale, cu = gen.batch_rows(w, self.lens, needles=needles)
         self.cu = cu
         rows = torch.from_numpy(data.view(np.uint8).reshape(len(data), -1)).to("cuda")
@@ -72,7 +73,7 @@ class Case:
         o, lse = OA.decode_attention(self.q_bits[b], kv, L, w.sm_scale, w.causal, w.lse_base)
         if not partials:
             return o, lse, None, None
-        op, lp = OA.rank_partials(self.q_bits[b], kv, L, w.sm_scale, w.c, w.causal, w.lse_base)
+        op, lp = OA.rank_partials(self.q_bits[b], kv, L, w.sm_scale, w.c, w.causal, w.lse_base, I=w.interleave)
         return o, lse, op, lp
 
 

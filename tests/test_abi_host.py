@@ -45,9 +45,9 @@ def test_status_strings(lib):
     assert dcp_status_string(12345) == "unknown status"
 
 
-def _layout(c=4, page=16, num_pages=10, kv=0):
+def _layout(c=4, page=16, num_pages=10, kv=0, interleave=1):
     from kv_sharded_mla_amd import make_layout
-    return make_layout(c, page, num_pages, kv)
+    return make_layout(c, page, num_pages, kv, interleave)
 
 
 def test_pool_bytes(lib):
@@ -56,6 +56,13 @@ def test_pool_bytes(lib):
     assert dcp_pool_bytes(_layout(4, 16, 10, 1)) == 10 * 16 * 576
     assert dcp_pool_bytes(_layout(0, 16, 10, 0)) == -1
     assert dcp_pool_bytes(_layout(4, 16, 10, 7)) == -1
+    # interleave size: a divisor of the page size; 0 reads as 1
+    assert dcp_pool_bytes(_layout(4, 16, 10, 0, 8)) == 10 * 16 * 1152
+    assert dcp_pool_bytes(_layout(4, 16, 10, 0, 16)) == 10 * 16 * 1152
+    assert dcp_pool_bytes(_layout(4, 16, 10, 0, 0)) == 10 * 16 * 1152
+    assert dcp_pool_bytes(_layout(4, 16, 10, 0, 3)) == -1
+    assert dcp_pool_bytes(_layout(4, 16, 10, 0, 32)) == -1
+    assert dcp_pool_bytes(_layout(4, 16, 10, 0, -2)) == -1
 
 
 def test_host_argument_errors(lib):
@@ -108,3 +115,8 @@ def test_workspace_size_covers_the_work_plan(lib):
     assert mla_decode_workspace_size(_layout(8, 1, 100, 0), 8, 64, 1, 16, 1 << 20) > \
         mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 64, 1, 16, 1 << 20)
     assert mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 4, 9, 64, 1000) == 0  # invalid -> 0
+    # runs of I positions per owner can only raise one rank's share of a request
+    for L in (100, 1000, 1 << 20):
+        assert mla_decode_workspace_size(_layout(8, 64, 100, 0, 64), 8, 64, 1, 16, L) >= \
+            mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 64, 1, 16, L)
+    assert mla_decode_workspace_size(_layout(8, 64, 100, 0, 48), 8, 64, 1, 16, 1000) == 0

@@ -4,7 +4,8 @@ Small cases span several LDS stages, ragged tails, empty shards (L < c),
 zero-length requests, every row-block shape (16/32/64 rows per workgroup and
 several blocks), q_len 4 causal verification, non-causal multi-row queries,
 base-2 LSE, pages that do not align with a stage, KV splits with their
-combine, and the e4m3 format.  Each compares every request's merged output
+combine, the e4m3 format, and interleave sizes I > 1 (runs of I positions
+per owner, including runs that leave whole ranks empty).  Each compares every request's merged output
 and every rank's partial with the oracle at the stated tolerances.
 """
 import numpy as np
@@ -44,6 +45,19 @@ CASES = [
     ("fp8_splits", W(index=68, H=64, c=1, P=64, fixed_len=40000, kv_dtype="fp8"), None),
     ("fp8_one_to_four_stages", W(index=72, H=32, c=1, P=64, B=5, kv_dtype="fp8"), [1, 40, 70, 100, 128]),
     ("fp8_empty_shards", W(index=73, H=64, c=8, P=16, fixed_len=5, kv_dtype="fp8"), None),
+    # interleave size I > 1: owners take runs of I consecutive positions
+    ("il16_h64", W(index=80, H=64, c=4, P=64, fixed_len=777, interleave=16), None),
+    ("il64_two_owners_of_eight", W(index=81, H=32, c=8, P=64, fixed_len=100, interleave=64), None),
+    ("il8_verify_q4", W(index=82, H=16, q_len=4, c=3, P=32, fixed_len=203, B=2, interleave=8), None),
+    ("il4_noncausal_q2", W(index=83, H=32, q_len=2, c=3, P=32, fixed_len=90, causal=False, interleave=4), None),
+    ("il32_splits", W(index=84, H=16, c=2, P=64, fixed_len=20000, interleave=32), None),
+    ("il8_ragged_batch", W(index=85, H=64, c=4, P=16, B=4, interleave=8), [1, 9, 500, 3001]),
+    ("il3_page48", W(index=86, H=16, c=3, P=48, fixed_len=700, interleave=3), None),
+    ("il16_h128_two_blocks", W(index=90, H=128, c=2, P=64, fixed_len=300, B=2, interleave=16), None),
+    ("fp8_il16", W(index=87, H=64, c=8, P=64, fixed_len=3000, kv_dtype="fp8", interleave=16), None),
+    ("fp8_il64_verify", W(index=88, H=32, q_len=4, c=4, P=64, fixed_len=1500, kv_dtype="fp8", B=2,
+                          interleave=64), None),
+    ("fp8_il8_short", W(index=89, H=16, c=8, P=16, fixed_len=37, kv_dtype="fp8", interleave=8), None),
 ]
 
 

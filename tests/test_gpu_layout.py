@@ -74,11 +74,15 @@ def test_alloc_errors_leave_state(old, new, top, stride, code):
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("seed", range(4))
-def test_kv_write_pool_bytes_exact(kv, seed):
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_kv_write_pool_bytes_exact(kv, seed, interleaved):
+    """Pool bytes and slots of dcp_kv_write equal the layout model's, round robin
+    (I = 1) and with runs of I positions per owner (I a divisor of P)."""
     K = _lib()
-    rng = np.random.default_rng(100 + seed)
+    rng = np.random.default_rng(100 + seed + 50 * interleaved)
     c = int(rng.integers(1, 9))
-    P = int(rng.choice([1, 3, 16, 64]))
+    P = int(rng.choice([4, 12, 16, 64] if interleaved else [1, 3, 16, 64]))
+    I = int(rng.choice([d for d in range(2, P + 1) if P % d == 0])) if interleaved else 1
     B = int(rng.integers(1, 12))
     lens = rng.integers(0, 700, size=B)
     vp = P * c
@@ -98,9 +102,9 @@ def test_kv_write_pool_bytes_exact(kv, seed):
     scales = rng.standard_normal(N).astype(np.float32) if fp8 else None
     pools = np.full((c, num_pages * P, elems), 0xEE if fp8 else 0xEEEE, dtype=row_dtype)
     pscales = np.full((c, num_pages * P), -1.5, np.float32) if fp8 else None
-    est, own, phys, want, want_sc = OL.pool_image(pools, bt, lens, cu, rows, P, c, scales, pscales)
+    est, own, phys, want, want_sc = OL.pool_image(pools, bt, lens, cu, rows, P, c, scales, pscales, I)
     assert est == OL.OK
-    layout = K.make_layout(c, P, num_pages, K.KV_FP8_E4M3 if fp8 else K.KV_BF16)
+    layout = K.make_layout(c, P, num_pages, K.KV_FP8_E4M3 if fp8 else K.KV_BF16, I)
     d_pools = torch.from_numpy(pools.view(np.uint8).reshape(-1).copy()).to("cuda")
     d_psc = _t(pscales.reshape(-1), torch.float32) if fp8 else None
     d_rows = torch.from_numpy(rows.view(np.uint8).reshape(N, -1).copy()).to("cuda")

@@ -39,6 +39,7 @@ class Workload:
     ragged: Optional[Tuple[Tuple[int, int, int], ...]] = None  # (count, lo, hi) log-uniform groups
     causal: bool = True
     sm_scale: float = SM_SCALE
+    interleave: int = 1   # KV interleave size I: runs of I consecutive positions per owner
     description: str = ""
 
     @property
@@ -86,11 +87,11 @@ BY_NAME = {w.name: w for w in ALL}
 
 
 def scaled(w: Workload, *, B=None, H=None, q_len=None, c=None, P=None, length=None,
-           kv_dtype=None, lse_base=None, causal=None, name=None) -> Workload:
+           kv_dtype=None, lse_base=None, causal=None, interleave=None, name=None) -> Workload:
     """A copy of ``w`` with some sizes replaced (used for small parity cases)."""
     kw = dict(w.__dict__)
     for k, v in dict(B=B, H=H, q_len=q_len, c=c, P=P, kv_dtype=kv_dtype, lse_base=lse_base,
-                     causal=causal).items():
+                     causal=causal, interleave=interleave).items():
         if v is not None:
             kw[k] = v
     if length is not None:
