@@ -170,3 +170,103 @@ def rank_local_slots(block_table_row: Sequence[int], length: int, P: int, c: int
                      I: int = 1) -> List[int]:
     """Physical slots, in rank r's pool, of the positions r owns, in position order."""
     return [slot_of(block_table_row, int(p), P, c, I)[1] for p in owned_positions(length, c, r, I)]
+
+
+# ---- extend and prefill->decode relayout ------------------------------------
+#
+# SGLang page "Decode Context Parallelism": the section on the decode cost
+# model says an extend step may gather the cached prefix shards back into
+# token order before appending new tokens; the section "DCP x PD
+# disaggregation" says dense prefill pages cannot be copied into striped decode
+# storage as they are, that a DCP1 prefill feeding a DCP-c decode relays the
+# tokens out, selecting and packing the rows each decode rank owns, and that
+# the plan carries the exact token count so that no stale row of a partly
+# filled last page is transferred.
+
+
+def read_rows(pools: np.ndarray, block_table: np.ndarray, seq_len: Sequence[int], cu_out: Sequence[int],
+              P: int, c: int, I: int = 1, pool_scales: np.ndarray = None, out: np.ndarray = None,
+              out_scales: np.ndarray = None):
+    """Rows of positions 0 .. seq_len[b]-1 of every request, in token order.
+
+    Row p of request b goes to ``out[cu_out[b] + p]``.  ``pools`` is
+    [c][num_pages*P][row elements].  A request with seq_len < 0 or
+    cu_out[b+1] - cu_out[b] != seq_len[b] is skipped (BAD_LENGTH), one that
+    needs more virtual pages than a table row holds is skipped
+    (TABLE_OVERFLOW), and a position on a page id outside the pools is skipped
+    (BAD_PAGE).  Skipped rows of ``out`` keep their contents.  Returns
+    ``(status, out, out_scales)``.
+    """
+    B = len(seq_len)
+    num_pages = pools.shape[1] // P
+    n_out = int(cu_out[B]) if out is None else out.shape[0]
+    if out is None:
+        out = np.zeros((n_out,) + pools.shape[2:], dtype=pools.dtype)
+    else:
+        out = np.array(out, copy=True)
+    if pool_scales is not None:
+        out_scales = np.zeros(n_out, np.float32) if out_scales is None else np.array(out_scales, copy=True)
+    stride = block_table.shape[1]
+    status = OK
+    for b in range(B):
+        L = int(seq_len[b])
+        if L < 0 or int(cu_out[b + 1]) - int(cu_out[b]) != L:
+            status = max(status, BAD_LENGTH)
+            continue
+        if pages_for(L, P, c) > stride:
+            status = max(status, TABLE_OVERFLOW)
+            continue
+        for p in range(L):
+            page = int(block_table[b, p // (P * c)])
+            if page < 0 or page >= num_pages:
+                status = max(status, BAD_PAGE)
+                continue
+            r, s = slot_of(block_table[b], p, P, c, I)
+            out[int(cu_out[b]) + p] = pools[r, s]
+            if pool_scales is not None:
+                out_scales[int(cu_out[b]) + p] = pool_scales[r, s]
+    return status, out, out_scales
+
+
+def relayout_dense(src_pool: np.ndarray, src_table: np.ndarray, seq_len: Sequence[int], P: int, c: int,
+                   dst_pools: np.ndarray, dst_table: np.ndarray, rank_begin: int, rank_count: int,
+                   I: int = 1, src_scales: np.ndarray = None, dst_scales: np.ndarray = None):
+    """Copy every request's rows from a dense (DCP1) paged pool into the owner pools.
+
+    The dense pool is [num_src_pages*P][row elements]; position p of request b
+    sits there at slot src_table[b][p // P] * P + p % P.  Exactly the
+    positions p < seq_len[b] whose owner is in [rank_begin, rank_begin +
+    rank_count) are written, at the slot the shared virtual table dst_table
+    gives them; nothing else in ``dst_pools`` changes.  Requests or positions
+    that fail a check are skipped as in :func:`read_rows` (a page id of
+    either table outside its pool: BAD_PAGE).  Returns ``(status, dst_pools,
+    dst_scales)``.
+    """
+    out = np.array(dst_pools, copy=True)
+    outs = None if dst_scales is None else np.array(dst_scales, copy=True)
+    n_src_pages = src_pool.shape[0] // P
+    num_pages = out.shape[1] // P
+    status = OK
+    for b in range(len(seq_len)):
+        L = int(seq_len[b])
+        if L < 0:
+            status = max(status, BAD_LENGTH)
+            continue
+        if (L + P - 1) // P > src_table.shape[1] or pages_for(L, P, c) > dst_table.shape[1]:
+            status = max(status, TABLE_OVERFLOW)
+            continue
+        for p in range(L):
+            # the owner does not depend on the page ids (I divides P): ranks
+            # outside the range neither read nor check anything
+            if not rank_begin <= owner(p, c, I) < rank_begin + rank_count:
+                continue
+            sp = int(src_table[b, p // P])
+            vpg = int(dst_table[b, p // (P * c)])
+            if sp < 0 or sp >= n_src_pages or vpg < 0 or vpg >= num_pages:
+                status = max(status, BAD_PAGE)
+                continue
+            r, s = slot_of(dst_table[b], p, P, c, I)
+            out[r, s] = src_pool[sp * P + p % P]
+            if outs is not None:
+                outs[r, s] = src_scales[sp * P + p % P]
+    return status, out, outs

@@ -218,3 +218,187 @@ def test_interleave_one_is_the_token_cycle():
     for v in range(200):
         for c in (1, 2, 3, 8):
             assert layout.owner(v, c, 1) == v % c and layout.physical(v, c, 1) == v // c
+
+
+# ---- extend gather (striped -> token order) and DCP1 -> DCP c relayout -------
+# Expected pools are built with the dealing model above (chunks of I positions
+# dealt rank after rank onto each rank's own page of the virtual page), with
+# page ids taken from the request's table; no closed form of the oracle is used.
+
+def _dealt_request(bt_row, L, P, c, I):
+    """position -> (rank, physical slot) of one request whose virtual pages are bt_row."""
+    out = {}
+    for g in range((L + P * c - 1) // (P * c)):
+        fill = [0] * c
+        pos, rank = g * P * c, 0
+        while pos < (g + 1) * P * c:
+            for _ in range(I):
+                if pos < L:
+                    out[pos] = (rank, int(bt_row[g]) * P + fill[rank])
+                fill[rank] += 1
+                pos += 1
+            rank = (rank + 1) % c
+    return out
+
+
+def _row(b, p, width=5):
+    return np.array([(b * 131 + p * 7 + k * 3) % 65521 for k in range(width)], dtype=np.uint16)
+
+
+def _striped_case(seed, c, P, I, lens):
+    rng = np.random.default_rng(seed)
+    vp = P * c
+    stride = max(1, max((L + vp - 1) // vp for L in lens))
+    num_pages = sum((L + vp - 1) // vp for L in lens) + 2
+    ids = rng.permutation(num_pages)
+    bt = np.full((len(lens), stride), -1, np.int32)
+    k = 0
+    for b, L in enumerate(lens):
+        for g in range((L + vp - 1) // vp):
+            bt[b, g] = ids[k]
+            k += 1
+    return bt, num_pages
+
+
+@pytest.mark.parametrize("c,P,I,lens", [
+    (4, 2, 1, [22, 0, 9]), (2, 4, 2, [17, 8]), (3, 6, 3, [40, 1, 18]), (8, 16, 4, [300]), (1, 4, 1, [13, 4]),
+    (4, 8, 8, [70, 33]),
+])
+def test_read_rows_restores_token_order(c, P, I, lens):
+    bt, num_pages = _striped_case(len(lens) + c, c, P, I, lens)
+    pools = np.full((c, num_pages * P, 5), 0xBEEF, np.uint16)
+    for b, L in enumerate(lens):
+        for p, (r, s) in _dealt_request(bt[b], L, P, c, I).items():
+            pools[r, s] = _row(b, p)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    st, out, _ = layout.read_rows(pools, bt, lens, cu, P, c, I)
+    assert st == layout.OK
+    want = np.array([_row(b, p) for b, L in enumerate(lens) for p in range(L)], dtype=np.uint16).reshape(-1, 5)
+    assert np.array_equal(out, want)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_read_rows_inverts_the_scatter(seed):
+    rng = np.random.default_rng(seed)
+    c = int(rng.integers(1, 6))
+    P = int(rng.choice([1, 4, 6, 16]))
+    I = int(rng.choice([d for d in range(1, P + 1) if P % d == 0]))
+    lens = [int(x) for x in rng.integers(0, 90, size=int(rng.integers(1, 5)))]
+    bt, num_pages = _striped_case(seed, c, P, I, lens)
+    rows = rng.integers(0, 65536, size=(sum(lens), 7)).astype(np.uint16)
+    scales = rng.standard_normal(sum(lens)).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    pools = np.zeros((c, num_pages * P, 7), np.uint16)
+    pscales = np.zeros((c, num_pages * P), np.float32)
+    st, _, _, pools, pscales = layout.pool_image(pools, bt, lens, cu, rows, P, c, scales, pscales, I)
+    assert st == layout.OK
+    st, out, out_sc = layout.read_rows(pools, bt, lens, cu, P, c, I, pool_scales=pscales)
+    assert st == layout.OK
+    assert np.array_equal(out, rows) and np.array_equal(out_sc, scales)
+
+
+def test_read_rows_errors_skip_and_keep():
+    c, P = 2, 2
+    bt = np.array([[0, 1], [1, -1], [5, 0]], np.int32)
+    pools = np.arange(c * 2 * P * 3, dtype=np.uint16).reshape(c, 2 * P, 3)
+    sentinel = np.full((9, 3), 0xEEEE, np.uint16)
+    # request 0 fine (5 tokens), request 1 has a length that disagrees with cu_out
+    st, out, _ = layout.read_rows(pools, bt, [5, 2, 0], [0, 5, 8, 8], P, c, out=sentinel[:8])
+    assert st == layout.BAD_LENGTH and (out[5:8] == 0xEEEE).all() and not (out[:5] == 0xEEEE).any()
+    # 9 tokens need 3 virtual pages of 4 > stride 2
+    st, out, _ = layout.read_rows(pools, bt, [9, 0, 0], [0, 9, 9, 9], P, c, out=sentinel)
+    assert st == layout.TABLE_OVERFLOW and (out == 0xEEEE).all()
+    # page id 5 is outside a 2-page pool: the 4 positions of that virtual page are skipped
+    st, out, _ = layout.read_rows(pools, bt, [0, 0, 6], [0, 0, 0, 6], P, c, out=sentinel[:6])
+    assert st == layout.BAD_PAGE and (out[:4] == 0xEEEE).all() and not (out[4:6] == 0xEEEE).any()
+
+
+def _dense_case(seed, c, P, I, lens):
+    """A DCP1 pool (pages of P in a shuffled order) holding _row(b, p), its table, and the
+    striped side's virtual table."""
+    rng = np.random.default_rng(seed)
+    n_src = sum((L + P - 1) // P for L in lens) + 1
+    sids = rng.permutation(n_src)
+    s_stride = max(1, max((L + P - 1) // P for L in lens))
+    src_bt = np.full((len(lens), s_stride), -1, np.int32)
+    src = np.full((n_src * P, 5), 0xDDDD, np.uint16)
+    k = 0
+    for b, L in enumerate(lens):
+        for q in range((L + P - 1) // P):
+            src_bt[b, q] = sids[k]
+            k += 1
+        for p in range(L):
+            src[src_bt[b, p // P] * P + p % P] = _row(b, p)
+    bt, num_pages = _striped_case(seed + 100, c, P, I, lens)
+    return src, src_bt, bt, num_pages
+
+
+@pytest.mark.parametrize("c,P,I,lens", [
+    (4, 2, 1, [22, 0, 9]), (2, 4, 2, [17, 8]), (3, 6, 3, [40, 1, 18]), (8, 16, 16, [300, 5]), (1, 4, 1, [13, 4]),
+])
+def test_relayout_places_exactly_the_owned_rows(c, P, I, lens):
+    src, src_bt, bt, num_pages = _dense_case(c * 10 + P, c, P, I, lens)
+    dst = np.full((c, num_pages * P, 5), 0xEEEE, np.uint16)
+    st, out, _ = layout.relayout_dense(src, src_bt, lens, P, c, dst, bt, 0, c, I)
+    assert st == layout.OK
+    written = set()
+    for b, L in enumerate(lens):
+        for p, (r, s) in _dealt_request(bt[b], L, P, c, I).items():
+            assert np.array_equal(out[r, s], _row(b, p)), (b, p)
+            written.add((r, s))
+    # the exact token count: every other slot, including the rest of a partly
+    # filled last page, keeps what it held
+    for r in range(c):
+        for s in range(num_pages * P):
+            if (r, s) not in written:
+                assert (out[r, s] == 0xEEEE).all()
+        got = sum(1 for (rr, _) in written if rr == r)
+        assert got == sum(layout.owned_count(L, c, r, I) for L in lens)
+
+
+def test_relayout_rank_ranges_compose():
+    c, P, I, lens = 4, 4, 2, [37, 12]
+    src, src_bt, bt, num_pages = _dense_case(3, c, P, I, lens)
+    dst = np.full((c, num_pages * P, 5), 0xEEEE, np.uint16)
+    _, whole, _ = layout.relayout_dense(src, src_bt, lens, P, c, dst, bt, 0, c, I)
+    part = dst
+    for r in range(c):
+        st, part, _ = layout.relayout_dense(src, src_bt, lens, P, c, part, bt, r, 1, I)
+        assert st == layout.OK
+        # one decode rank's call writes its own pool only
+        _, alone, _ = layout.relayout_dense(src, src_bt, lens, P, c, dst, bt, r, 1, I)
+        for o in range(c):
+            assert np.array_equal(alone[o], whole[o] if o == r else dst[o])
+    assert np.array_equal(part, whole)
+
+
+def test_relayout_to_one_rank_is_the_page_copy():
+    # equal DCP sizes (1 and 1) take the existing page path: with the same table the
+    # destination pages are the source pages, row for row, over each request's length
+    P, lens = 4, [10, 3]
+    src, src_bt, _, _ = _dense_case(5, 1, P, 1, lens)
+    dst = np.full((1,) + src.shape, 0xEEEE, np.uint16)
+    st, out, _ = layout.relayout_dense(src, src_bt, lens, P, 1, dst, src_bt, 0, 1, 1)
+    assert st == layout.OK
+    for b, L in enumerate(lens):
+        for p in range(L):
+            slot = src_bt[b, p // P] * P + p % P
+            assert np.array_equal(out[0, slot], src[slot])
+
+
+def test_relayout_errors():
+    c, P, I, lens = 2, 4, 4, [16]
+    src, src_bt, bt, num_pages = _dense_case(9, c, P, I, lens)
+    dst = np.full((c, num_pages * P, 5), 0xEEEE, np.uint16)
+    st, out, _ = layout.relayout_dense(src, src_bt, [-1], P, c, dst, bt, 0, c, I)
+    assert st == layout.BAD_LENGTH and np.array_equal(out, dst)
+    st, out, _ = layout.relayout_dense(src, src_bt[:, :2], [16], P, c, dst, bt, 0, c, I)
+    assert st == layout.TABLE_OVERFLOW and np.array_equal(out, dst)
+    # with I = P each source page belongs to one rank: a bad page of rank 1 is an error
+    # for a call that covers rank 1 and invisible to one that covers rank 0 only
+    bad = src_bt.copy()
+    bad[0, 1] = 99          # positions 4..7, owned by rank 1
+    st, out, _ = layout.relayout_dense(src, bad, [16], P, c, dst, bt, 0, c, I)
+    assert st == layout.BAD_PAGE
+    st, out0, _ = layout.relayout_dense(src, bad, [16], P, c, dst, bt, 0, 1, I)
+    assert st == layout.OK and np.array_equal(out0[1], dst[1])
