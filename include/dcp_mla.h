@@ -223,6 +223,73 @@ int mla_decode_partial(const dcp_layout* layout, const void* pools, const float*
 int dcp_lse_merge(int32_t c, int64_t rows, const float* o_part, const float* lse_part,
                   int32_t lse_base, void* o_out, float* lse_out, hipStream_t stream);
 
+/*
+ * dcp_kv_read - gather every request's cached rows back into token order.
+ *
+ * SGLang "Decode Context Parallelism", decode cost model: an extend step,
+ * which lies outside that model, may gather the cached prefix shards,
+ * restore token order and then append the new tokens (dcp_kv_write).
+ *
+ * Position p (0 <= p < seq_len[b]) of request b is read from its owner pool
+ * (slot as in dcp_kv_write, interleave included) and written to row
+ * cu_out[b] + p of rows_out; bytes are copied unchanged (plus the e4m3
+ * scale to scales_out).  A request with seq_len[b] < 0, with cu_out[b+1] -
+ * cu_out[b] != seq_len[b] or with a span outside [0, n_rows) is skipped
+ * (DCP_DEV_BAD_LENGTH), one that needs more than bt_stride virtual pages
+ * too (DCP_DEV_TABLE_OVERFLOW), and so are the positions of a virtual page
+ * whose id is outside [0, num_pages) (DCP_DEV_BAD_PAGE).  Rows not written
+ * keep their bytes.
+ *
+ *   pools        c pools (see layout above), read only
+ *   pool_scales  float32 [c][num_pages*page] for e4m3, else NULL
+ *   seq_len      int32 [batch]; cu_out int32 [batch+1]
+ *   rows_out     [n_rows][576] bf16 or e4m3 (16-byte aligned)
+ *   scales_out   float32 [n_rows] for e4m3, else NULL
+ * batch <= 65536; page * c <= 2^30 (else DCP_ERR_UNSUPPORTED).
+ */
+int dcp_kv_read(const dcp_layout* layout, const void* pools, const float* pool_scales,
+                const int32_t* block_table, int32_t bt_stride, const int32_t* seq_len,
+                const int32_t* cu_out, int32_t batch, int64_t n_rows, void* rows_out,
+                float* scales_out, int32_t* dev_status, hipStream_t stream);
+
+/*
+ * dcp_kv_relayout - copy dense (DCP size 1) paged KV into striped owner pools.
+ *
+ * SGLang "Decode Context Parallelism", section "DCP x PD disaggregation":
+ * dense prefill pages cannot be copied into striped decode storage as they
+ * are; going from a DCP1 prefill to a DCP decode relays the tokens out,
+ * selecting for each decode rank the rows it owns, and the exact token count
+ * keeps stale rows of a partly filled last page out.
+ *
+ * The source is one pool of src_num_pages pages of `page` tokens in the
+ * layout's KV dtype; position p of request b sits at slot
+ * src_block_table[b][p / page] * page + p mod page.  For every p <
+ * seq_len[b] whose owner (as in dcp_kv_write) is in [rank_begin, rank_begin
+ * + rank_count), the row (and e4m3 scale) is copied to its slot in that
+ * owner's pool through the shared virtual table block_table, which must
+ * already hold the request's virtual pages (dcp_alloc_virtual).  Nothing
+ * else is written: not the other ranks' rows, not the slots of a last page
+ * past the request's length.  A request with seq_len[b] < 0 is skipped
+ * (DCP_DEV_BAD_LENGTH), one whose pages do not fit either table too
+ * (DCP_DEV_TABLE_OVERFLOW); a position whose page id in either table is
+ * outside its pool is skipped (DCP_DEV_BAD_PAGE).  pools (and pool_scales)
+ * hold the pools of ranks rank_begin .. rank_begin + rank_count - 1 back to
+ * back, as in mla_decode_partial: a real decode rank r passes rank_begin = r,
+ * rank_count = 1 and its own pool; the emulated group on one GPU passes 0,
+ * c and all c pools.
+ *
+ *   src_pool       [src_num_pages*page][576] bf16 or e4m3, read only
+ *   src_scales     float32 [src_num_pages*page] for e4m3, else NULL
+ *   src_block_table int32 [batch][src_bt_stride]
+ *   pools, pool_scales, block_table, bt_stride: as in dcp_kv_write
+ * batch <= 65536; page * c <= 2^30 (else DCP_ERR_UNSUPPORTED).
+ */
+int dcp_kv_relayout(const dcp_layout* layout, const void* src_pool, const float* src_scales,
+                    int32_t src_num_pages, const int32_t* src_block_table, int32_t src_bt_stride,
+                    const int32_t* seq_len, int32_t batch, int32_t rank_begin, int32_t rank_count,
+                    void* pools, float* pool_scales, const int32_t* block_table, int32_t bt_stride,
+                    int32_t* dev_status, hipStream_t stream);
+
 /* Static description of a status value (host or device code). */
 const char* dcp_status_string(int status);
 

@@ -57,6 +57,9 @@ _SIGS = {
     "dcp_pool_bytes": (_I64, [_PL]),
     "dcp_alloc_virtual": (ctypes.c_int, [_PL, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _VP, _VP]),
     "dcp_kv_write": (ctypes.c_int, [_PL, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I64, _VP, _VP, _VP, _VP, _VP]),
+    "dcp_kv_read": (ctypes.c_int, [_PL, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I64, _VP, _VP, _VP, _VP]),
+    "dcp_kv_relayout": (ctypes.c_int, [_PL, _VP, _VP, _I32, _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _I32,
+                                       _VP, _VP]),
     "mla_decode_workspace_size": (ctypes.c_size_t, [_PL, _I32, _I32, _I32, _I32, _I64]),
     "mla_decode_partial": (ctypes.c_int, [_PL, _VP, _VP, _I32, _I32, _VP, _I32, _I32, _I32, _VP, _I32, _VP,
                                           _I64, ctypes.c_float, _I32, _I32, _VP, _VP, _VP, ctypes.c_size_t,
@@ -146,6 +149,37 @@ def dcp_kv_write(layout: Layout, pools, pool_scales, block_table, seq_len, cu_ne
         _ptr(row_scales, "row_scales", torch.float32), _ptr(slot_out, "slot_out", torch.int64),
         _ptr(dev_status, "dev_status", torch.int32, 1), _stream(stream))
     _check("dcp_kv_write", st)
+
+
+def dcp_kv_read(layout: Layout, pools, pool_scales, block_table, seq_len, cu_out, rows_out, scales_out=None,
+                dev_status=None, stream=None):
+    """Gather positions 0 .. seq_len[b]-1 of every request into rows_out[cu_out[b] + p] (token order)."""
+    B = seq_len.numel()
+    payload = (torch.uint8, torch.int16, torch.bfloat16)
+    st = load_library().dcp_kv_read(
+        ctypes.byref(layout), _ptr(pools, "pools", payload), _ptr(pool_scales, "pool_scales", torch.float32),
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[-1], _ptr(seq_len, "seq_len", torch.int32),
+        _ptr(cu_out, "cu_out", torch.int32, B + 1), B, rows_out.shape[0], _ptr(rows_out, "rows_out", payload),
+        _ptr(scales_out, "scales_out", torch.float32), _ptr(dev_status, "dev_status", torch.int32, 1),
+        _stream(stream))
+    _check("dcp_kv_read", st)
+
+
+def dcp_kv_relayout(layout: Layout, src_pool, src_scales, src_block_table, seq_len, rank_begin: int,
+                    rank_count: int, pools, pool_scales, block_table, dev_status=None, stream=None):
+    """Copy the rows of ranks [rank_begin, rank_begin + rank_count) from a dense paged pool
+    (pages of layout.page tokens) into their owner pools (those ranks' pools, back to back)."""
+    B = seq_len.numel()
+    payload = (torch.uint8, torch.int16, torch.bfloat16)
+    row_bytes = D_QK if layout.kv_dtype == KV_FP8_E4M3 else 2 * D_QK
+    src_pages = src_pool.numel() * src_pool.element_size() // (row_bytes * layout.page)
+    st = load_library().dcp_kv_relayout(
+        ctypes.byref(layout), _ptr(src_pool, "src_pool", payload), _ptr(src_scales, "src_scales", torch.float32),
+        src_pages, _ptr(src_block_table, "src_block_table", torch.int32), src_block_table.shape[-1],
+        _ptr(seq_len, "seq_len", torch.int32), B, int(rank_begin), int(rank_count), _ptr(pools, "pools", payload),
+        _ptr(pool_scales, "pool_scales", torch.float32), _ptr(block_table, "block_table", torch.int32),
+        block_table.shape[-1], _ptr(dev_status, "dev_status", torch.int32, 1), _stream(stream))
+    _check("dcp_kv_relayout", st)
 
 
 def mla_decode_workspace_size(layout: Layout, rank_count: int, batch: int, q_len: int, heads: int,

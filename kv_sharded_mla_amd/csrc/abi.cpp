@@ -68,6 +68,44 @@ int dcp_kv_write(const dcp_layout* layout, void* pools, float* pool_scales, cons
                                          slot_out, dev_status, stream));
 }
 
+int dcp_kv_read(const dcp_layout* layout, const void* pools, const float* pool_scales, const int32_t* block_table,
+                int32_t bt_stride, const int32_t* seq_len, const int32_t* cu_out, int32_t batch, int64_t n_rows,
+                void* rows_out, float* scales_out, int32_t* dev_status, hipStream_t stream) {
+  if (int s = check_layout(layout)) return s;
+  const bool fp8 = layout->kv_dtype == DCP_KV_FP8_E4M3;
+  if (batch < 0 || batch > 65536 || n_rows < 0 || bt_stride < 1) return DCP_ERR_INVALID_ARG;
+  if ((int64_t)layout->page * layout->c > (1 << 30)) return DCP_ERR_UNSUPPORTED;
+  if (batch == 0) return DCP_OK;
+  if (!pools || !block_table || !seq_len || !cu_out || (n_rows > 0 && !rows_out)) return DCP_ERR_INVALID_ARG;
+  if (fp8 && (!pool_scales || (n_rows > 0 && !scales_out))) return DCP_ERR_INVALID_ARG;
+  if (!aligned(pools, 16) || !aligned(rows_out, 16)) return DCP_ERR_ALIGNMENT;
+  if (fp8 && (!aligned(pool_scales, 4) || !aligned(scales_out, 4))) return DCP_ERR_ALIGNMENT;
+  return hip_status(dcp::launch_kv_read(layout->c, interleave_of(layout), layout->page, layout->num_pages, fp8, pools,
+                                        pool_scales, block_table, bt_stride, seq_len, cu_out, batch, n_rows, rows_out,
+                                        scales_out, dev_status, stream));
+}
+
+int dcp_kv_relayout(const dcp_layout* layout, const void* src_pool, const float* src_scales, int32_t src_num_pages,
+                    const int32_t* src_block_table, int32_t src_bt_stride, const int32_t* seq_len, int32_t batch,
+                    int32_t rank_begin, int32_t rank_count, void* pools, float* pool_scales,
+                    const int32_t* block_table, int32_t bt_stride, int32_t* dev_status, hipStream_t stream) {
+  if (int s = check_layout(layout)) return s;
+  const bool fp8 = layout->kv_dtype == DCP_KV_FP8_E4M3;
+  if (batch < 0 || batch > 65536 || bt_stride < 1 || src_bt_stride < 1 || src_num_pages < 0) return DCP_ERR_INVALID_ARG;
+  if (rank_begin < 0 || rank_count < 1 || (int64_t)rank_begin + rank_count > layout->c) return DCP_ERR_INVALID_ARG;
+  if ((int64_t)layout->page * layout->c > (1 << 30)) return DCP_ERR_UNSUPPORTED;
+  if ((int64_t)src_num_pages * layout->page > ((int64_t)1 << 40)) return DCP_ERR_UNSUPPORTED;
+  if (batch == 0) return DCP_OK;
+  if (!src_pool || !src_block_table || !seq_len || !pools || !block_table) return DCP_ERR_INVALID_ARG;
+  if (fp8 && (!src_scales || !pool_scales)) return DCP_ERR_INVALID_ARG;
+  if (!aligned(src_pool, 16) || !aligned(pools, 16)) return DCP_ERR_ALIGNMENT;
+  if (fp8 && (!aligned(src_scales, 4) || !aligned(pool_scales, 4))) return DCP_ERR_ALIGNMENT;
+  return hip_status(dcp::launch_kv_relayout(layout->c, interleave_of(layout), layout->page, layout->num_pages, fp8,
+                                            src_pool, src_scales, src_num_pages, src_block_table, src_bt_stride,
+                                            seq_len, batch, rank_begin, rank_count, pools, pool_scales, block_table,
+                                            bt_stride, dev_status, stream));
+}
+
 size_t mla_decode_workspace_size(const dcp_layout* layout, int32_t rank_count, int32_t batch, int32_t q_len,
                                  int32_t heads, int64_t max_seq_len) {
   if (check_layout(layout) != DCP_OK || rank_count < 1 || batch < 0 || q_len < 1 || q_len > DCP_MAX_Q_LEN ||

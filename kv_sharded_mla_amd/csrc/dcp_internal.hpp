@@ -18,6 +18,18 @@ hipError_t launch_kv_write(int32_t c, int32_t interleave, int32_t page, int32_t 
                            int64_t n_rows, const void* rows, const float* row_scales,
                            int64_t* slot_out, int32_t* dev_status, hipStream_t stream);
 
+hipError_t launch_kv_read(int32_t c, int32_t interleave, int32_t page, int32_t num_pages, bool fp8, const void* pools,
+                          const float* pool_scales, const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* seq_len, const int32_t* cu_out, int32_t batch, int64_t n_rows,
+                          void* rows_out, float* scales_out, int32_t* dev_status, hipStream_t stream);
+
+hipError_t launch_kv_relayout(int32_t c, int32_t interleave, int32_t page, int32_t num_pages, bool fp8,
+                              const void* src_pool, const float* src_scales, int32_t src_num_pages,
+                              const int32_t* src_table, int32_t src_stride, const int32_t* seq_len, int32_t batch,
+                              int32_t rank_begin, int32_t rank_count, void* pools, float* pool_scales,
+                              const int32_t* block_table, int32_t bt_stride, int32_t* dev_status,
+                              hipStream_t stream);
+
 hipError_t launch_lse_merge(int32_t c, int64_t rows, const float* o_part, const float* lse_part,
                             bool base2, void* o_out, float* lse_out, hipStream_t stream);
 

@@ -144,6 +144,161 @@ kv_write_kernel(int32_t c, int32_t il, int32_t page, int32_t num_pages, uint8_t*
   }
 }
 
+// ---- extend gather and DCP1 -> DCP c relayout -------------------------------
+// Both walk one virtual page of one request per step: rank r's P slots of
+// virtual page g (page id pg) sit contiguously in pool r at [pg*P, pg*P + P),
+// and local slot s there holds position g*P*c + (s / I)*I*c + r*I + s mod I.
+// Each wave copies whole rows (rows are wave-uniform, so the index arithmetic
+// is scalar), RPW rows per round with all loads issued before the stores.
+// Workgroup (b, k) of a batch x G grid takes virtual pages k, k + G, ... of
+// request b.
+
+constexpr int kCopyThreads = 256;
+constexpr int kRowsPerWave = 4;
+
+// position of local slot s of rank r in virtual page g
+__device__ __forceinline__ int64_t slot_position(int64_t g, int32_t s, int32_t r, int32_t c, int32_t il, int32_t page) {
+  return g * page * c + (int64_t)(s / il) * il * c + (int64_t)r * il + s % il;
+}
+
+// Lane l moves chunk l of each row and, for 72-chunk rows, lanes 0..7 also
+// chunk 64 + l; lanes past the row's chunks load an in-row chunk and store
+// nothing.
+template <bool FP8>
+__device__ __forceinline__ void copy_rows(const uint8_t* (&src)[kRowsPerWave], uint8_t* (&dst)[kRowsPerWave],
+                                          const bool (&live)[kRowsPerWave], int lane) {
+  static_assert(kRowsPerWave == 4, "four named rows below");
+  constexpr int kChunks = (FP8 ? kDqk : 2 * kDqk) / 16;   // 36 or 72 chunks of 16 bytes
+  constexpr int kTail = kChunks > 64 ? kChunks - 64 : 0;
+  const int c0 = lane < kChunks ? lane : 0;
+  const int c1 = 64 + (lane < kTail ? lane : 0);
+  // named registers rather than arrays: the loads of all four rows are in
+  // flight before the first store
+  auto ld = [&](int i, int4& x, int4& y) {
+    if (!live[i]) return;
+    x = reinterpret_cast<const int4*>(src[i])[c0];
+    if (kTail) y = reinterpret_cast<const int4*>(src[i])[c1];
+  };
+  auto st = [&](int i, const int4& x, const int4& y) {
+    if (!live[i]) return;
+    if (lane < kChunks) reinterpret_cast<int4*>(dst[i])[lane] = x;
+    if (kTail && lane < kTail) reinterpret_cast<int4*>(dst[i])[64 + lane] = y;
+  };
+  int4 a0 = {}, a1 = {}, a2 = {}, a3 = {}, t0 = {}, t1 = {}, t2 = {}, t3 = {};
+  ld(0, a0, t0);
+  ld(1, a1, t1);
+  ld(2, a2, t2);
+  ld(3, a3, t3);
+  st(0, a0, t0);
+  st(1, a1, t1);
+  st(2, a2, t2);
+  st(3, a3, t3);
+}
+
+template <bool FP8>
+__global__ void __launch_bounds__(kCopyThreads)
+kv_read_kernel(int32_t c, int32_t il, int32_t page, int32_t num_pages, int32_t G, const uint8_t* __restrict__ pools,
+               const float* __restrict__ pool_scales, const int32_t* __restrict__ block_table, int32_t bt_stride,
+               const int32_t* __restrict__ seq_len, const int32_t* __restrict__ cu_out, int64_t n_rows,
+               uint8_t* __restrict__ rows_out, float* __restrict__ scales_out, int32_t* __restrict__ dev_status) {
+  constexpr int64_t kRowBytes = FP8 ? kDqk : 2 * kDqk;
+  const int b = blockIdx.x / G, k = blockIdx.x % G;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t vpage = (int64_t)page * c;
+  const int64_t cap = (int64_t)num_pages * page;
+  const int32_t L = seq_len[b];
+  if (L < 0 || cu_out[b] < 0 || cu_out[b + 1] > n_rows || (int64_t)cu_out[b + 1] - cu_out[b] != L) {
+    if (k == 0 && threadIdx.x == 0 && dev_status) atomicMax(dev_status, DCP_DEV_BAD_LENGTH);
+    return;
+  }
+  const int64_t n_vp = (L + vpage - 1) / vpage;
+  if (n_vp > bt_stride) {
+    if (k == 0 && threadIdx.x == 0 && dev_status) atomicMax(dev_status, DCP_DEV_TABLE_OVERFLOW);
+    return;
+  }
+  uint8_t* out_b = rows_out + (int64_t)cu_out[b] * kRowBytes;
+  const int32_t per_vp = page * c;   // rows of one virtual page, taken rank by rank
+  for (int64_t g = k; g < n_vp; g += G) {
+    const int32_t pg = block_table[(int64_t)b * bt_stride + g];
+    if (pg < 0 || pg >= num_pages) {
+      if (threadIdx.x == 0 && dev_status) atomicMax(dev_status, DCP_DEV_BAD_PAGE);
+      continue;
+    }
+    for (int32_t i0 = wv * kRowsPerWave; i0 < per_vp; i0 += (kCopyThreads / 64) * kRowsPerWave) {
+      const uint8_t* src[kRowsPerWave];
+      uint8_t* dst[kRowsPerWave];
+      bool live[kRowsPerWave];
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        const int32_t rl = i0 + i;
+        const int32_t r = rl / page, s = rl - r * page;
+        const int64_t pos = slot_position(g, s, r, c, il, page);
+        live[i] = rl < per_vp && pos < L;
+        const int64_t slot = (int64_t)pg * page + s;
+        src[i] = pools + ((int64_t)r * cap + slot) * kRowBytes;
+        dst[i] = out_b + pos * kRowBytes;
+        if (FP8 && live[i] && lane == 0) scales_out[cu_out[b] + pos] = pool_scales[(int64_t)r * cap + slot];
+      }
+      copy_rows<FP8>(src, dst, live, lane);
+    }
+  }
+}
+
+template <bool FP8>
+__global__ void __launch_bounds__(kCopyThreads)
+kv_relayout_kernel(int32_t c, int32_t il, int32_t page, int32_t num_pages, int32_t G, int32_t rank_begin,
+                   int32_t rank_count, const uint8_t* __restrict__ src_pool, const float* __restrict__ src_scales,
+                   int32_t src_num_pages, const int32_t* __restrict__ src_table, int32_t src_stride,
+                   const int32_t* __restrict__ seq_len, uint8_t* __restrict__ pools, float* __restrict__ pool_scales,
+                   const int32_t* __restrict__ block_table, int32_t bt_stride, int32_t* __restrict__ dev_status) {
+  constexpr int64_t kRowBytes = FP8 ? kDqk : 2 * kDqk;
+  const int b = blockIdx.x / G, k = blockIdx.x % G;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t vpage = (int64_t)page * c;
+  const int64_t cap = (int64_t)num_pages * page;
+  const int32_t L = seq_len[b];
+  if (L < 0) {
+    if (k == 0 && threadIdx.x == 0 && dev_status) atomicMax(dev_status, DCP_DEV_BAD_LENGTH);
+    return;
+  }
+  const int64_t n_vp = (L + vpage - 1) / vpage;
+  if (n_vp > bt_stride || ((int64_t)L + page - 1) / page > src_stride) {
+    if (k == 0 && threadIdx.x == 0 && dev_status) atomicMax(dev_status, DCP_DEV_TABLE_OVERFLOW);
+    return;
+  }
+  const int32_t* st = src_table + (int64_t)b * src_stride;
+  const int32_t per_vp = page * rank_count;   // rows of the covered ranks in one virtual page
+  for (int64_t g = k; g < n_vp; g += G) {
+    const int32_t pg = block_table[(int64_t)b * bt_stride + g];
+    for (int32_t i0 = wv * kRowsPerWave; i0 < per_vp; i0 += (kCopyThreads / 64) * kRowsPerWave) {
+      const uint8_t* src[kRowsPerWave];
+      uint8_t* dst[kRowsPerWave];
+      bool live[kRowsPerWave];
+      int code = DCP_DEV_OK;
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        const int32_t rl = i0 + i;
+        const int32_t rr = rl / page, s = rl - rr * page;
+        const int32_t r = rank_begin + rr;
+        const int64_t pos = slot_position(g, s, r, c, il, page);
+        live[i] = rl < per_vp && pos < L;
+        const int32_t sp = live[i] ? st[pos / page] : 0;
+        if (live[i] && (sp < 0 || sp >= src_num_pages || pg < 0 || pg >= num_pages)) {
+          code = DCP_DEV_BAD_PAGE;
+          live[i] = false;
+        }
+        const int64_t slot = (int64_t)pg * page + s;
+        const int64_t sslot = (int64_t)sp * page + pos % page;
+        src[i] = src_pool + sslot * kRowBytes;
+        dst[i] = pools + ((int64_t)rr * cap + slot) * kRowBytes;
+        if (FP8 && live[i] && lane == 0) pool_scales[(int64_t)rr * cap + slot] = src_scales[sslot];
+      }
+      if (code != DCP_DEV_OK && lane == 0 && dev_status) atomicMax(dev_status, code);
+      copy_rows<FP8>(src, dst, live, lane);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_alloc_virtual(int32_t c, int32_t page, const int32_t* free_stack, int32_t* free_top,
@@ -171,6 +326,56 @@ hipError_t launch_kv_write(int32_t c, int32_t interleave, int32_t page, int32_t 
     hipLaunchKernelGGL(kv_write_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, c, interleave, page, num_pages,
                        (uint8_t*)pools, pool_scales, block_table, bt_stride, seq_len, cu_new, batch, n_rows,
                        (const uint8_t*)rows, row_scales, slot_out, dev_status);
+  return hipGetLastError();
+}
+
+}  // namespace dcp
+
+namespace dcp {
+
+namespace {
+// workgroups per request: enough in all for a few per CU, at most one per virtual page
+int32_t copy_split(int32_t batch, int32_t bt_stride) {
+  const int32_t want = (4096 + batch - 1) / batch;
+  return want < 1 ? 1 : (want > bt_stride ? bt_stride : want);
+}
+}  // namespace
+
+hipError_t launch_kv_read(int32_t c, int32_t interleave, int32_t page, int32_t num_pages, bool fp8, const void* pools,
+                          const float* pool_scales, const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* seq_len, const int32_t* cu_out, int32_t batch, int64_t n_rows,
+                          void* rows_out, float* scales_out, int32_t* dev_status, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  const int32_t G = copy_split(batch, bt_stride);
+  const dim3 grid((unsigned)((int64_t)batch * G)), block(kCopyThreads);
+  if (fp8)
+    hipLaunchKernelGGL(kv_read_kernel<true>, grid, block, 0, stream, c, interleave, page, num_pages, G,
+                       (const uint8_t*)pools, pool_scales, block_table, bt_stride, seq_len, cu_out, n_rows,
+                       (uint8_t*)rows_out, scales_out, dev_status);
+  else
+    hipLaunchKernelGGL(kv_read_kernel<false>, grid, block, 0, stream, c, interleave, page, num_pages, G,
+                       (const uint8_t*)pools, pool_scales, block_table, bt_stride, seq_len, cu_out, n_rows,
+                       (uint8_t*)rows_out, scales_out, dev_status);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_relayout(int32_t c, int32_t interleave, int32_t page, int32_t num_pages, bool fp8,
+                              const void* src_pool, const float* src_scales, int32_t src_num_pages,
+                              const int32_t* src_table, int32_t src_stride, const int32_t* seq_len, int32_t batch,
+                              int32_t rank_begin, int32_t rank_count, void* pools, float* pool_scales,
+                              const int32_t* block_table, int32_t bt_stride, int32_t* dev_status,
+                              hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  const int32_t G = copy_split(batch, bt_stride);
+  const dim3 grid((unsigned)((int64_t)batch * G)), block(kCopyThreads);
+  if (fp8)
+    hipLaunchKernelGGL(kv_relayout_kernel<true>, grid, block, 0, stream, c, interleave, page, num_pages, G,
+                       rank_begin, rank_count, (const uint8_t*)src_pool, src_scales, src_num_pages, src_table,
+                       src_stride, seq_len, (uint8_t*)pools, pool_scales, block_table, bt_stride, dev_status);
+  else
+    hipLaunchKernelGGL(kv_relayout_kernel<false>, grid, block, 0, stream, c, interleave, page, num_pages, G,
+                       rank_begin, rank_count, (const uint8_t*)src_pool, src_scales, src_num_pages, src_table,
+                       src_stride, seq_len, (uint8_t*)pools, pool_scales, block_table, bt_stride, dev_status);
   return hipGetLastError();
 }
 

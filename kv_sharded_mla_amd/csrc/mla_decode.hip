@@ -48,6 +48,10 @@ constexpr int kMaxTab = 512;  // page ids staged per workgroup
 constexpr int kStageTok = 32; // tokens per LDS stage
 // score fragments in token-block-major order (each accumulator then takes its
 // MFMAs back to back) or interleaved
+// work items the plan aims for per CU and row block
+#ifndef DCP_ITEMS_PER_CU
+#define DCP_ITEMS_PER_CU 2
+#endif
 #ifndef DCP_FP8_SCALE_PREFETCH
 #define DCP_FP8_SCALE_PREFETCH 0
 #endif
@@ -862,7 +866,7 @@ DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, in
   const int64_t stages_max = (n_r_max + kStageTok - 1) / kStageTok;
   pl.t_max = (int32_t)std::max<int64_t>(1, (int64_t)(kMaxTab - 1) * page / kStageTok);
   pl.t_min = std::min<int32_t>(8, pl.t_max);
-  pl.items_target = std::max<int32_t>(1, 2 * device_cu_count() / pl.n_row_blocks);
+  pl.items_target = std::max<int32_t>(1, DCP_ITEMS_PER_CU * device_cu_count() / pl.n_row_blocks);
   // the device plan makes at most units + max(items_target, units * ceil(stages_max / t_max)) items
   pl.max_items = pl.units + std::max<int64_t>(pl.items_target, pl.units * ((stages_max + pl.t_max - 1) / pl.t_max));
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };

@@ -190,8 +190,9 @@ def read_rows(pools: np.ndarray, block_table: np.ndarray, seq_len: Sequence[int]
     """Rows of positions 0 .. seq_len[b]-1 of every request, in token order.
 
     Row p of request b goes to ``out[cu_out[b] + p]``.  ``pools`` is
-    [c][num_pages*P][row elements].  A request with seq_len < 0 or
-    cu_out[b+1] - cu_out[b] != seq_len[b] is skipped (BAD_LENGTH), one that
+    [c][num_pages*P][row elements].  A request with seq_len < 0, with
+    cu_out[b+1] - cu_out[b] != seq_len[b], or whose span [cu_out[b],
+    cu_out[b+1]) leaves the output rows is skipped (BAD_LENGTH), one that
     needs more virtual pages than a table row holds is skipped
     (TABLE_OVERFLOW), and a position on a page id outside the pools is skipped
     (BAD_PAGE).  Skipped rows of ``out`` keep their contents.  Returns
@@ -210,7 +211,7 @@ def read_rows(pools: np.ndarray, block_table: np.ndarray, seq_len: Sequence[int]
     status = OK
     for b in range(B):
         L = int(seq_len[b])
-        if L < 0 or int(cu_out[b + 1]) - int(cu_out[b]) != L:
+        if L < 0 or int(cu_out[b]) < 0 or int(cu_out[b + 1]) > n_out or int(cu_out[b + 1]) - int(cu_out[b]) != L:
             status = max(status, BAD_LENGTH)
             continue
         if pages_for(L, P, c) > stride:

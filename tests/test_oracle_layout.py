@@ -402,3 +402,14 @@ def test_relayout_errors():
     assert st == layout.BAD_PAGE
     st, out0, _ = layout.relayout_dense(src, bad, [16], P, c, dst, bt, 0, 1, I)
     assert st == layout.OK and np.array_equal(out0[1], dst[1])
+
+
+def test_read_rows_span_outside_the_output_is_skipped():
+    c, P = 2, 2
+    bt = np.array([[0, 1]], np.int32)
+    pools = np.arange(c * 2 * P * 3, dtype=np.uint16).reshape(c, 2 * P, 3)
+    sentinel = np.full((4, 3), 0xEEEE, np.uint16)
+    st, out, _ = layout.read_rows(pools, bt, [3], [2, 5], P, c, out=sentinel)
+    assert st == layout.BAD_LENGTH and (out == 0xEEEE).all()
+    st, out, _ = layout.read_rows(pools, bt, [3], [1, 4], P, c, out=sentinel)
+    assert st == layout.OK and (out[0] == 0xEEEE).all() and not (out[1:] == 0xEEEE).any()
