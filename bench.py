@@ -11,6 +11,11 @@ in alternation so consecutive steps never find the previous step's KV in the
 Prints one JSON line (rank 0).  Progress goes to stderr.
 
     python bench.py [--config tplocal] [--steps K] [--warmup W] [--gpus 1]
+
+With --op read or --op relayout it times instead the extend gather
+(dcp_kv_read: all cached rows of the workload back to token order) or the
+DCP1 -> DCP c relayout (dcp_kv_relayout: a dense paged pool of the
+workload's context into the c owner pools), both byte copies bound by HBM.
 """
 from __future__ import annotations
 
@@ -38,6 +43,21 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, "kv_sharded_mla_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def load_copy_traffic(op: str, cfg_name: str):
+    """HBM traffic per layout-copy launch from a committed counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", f"kv_{op}_{cfg_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "kv_sharded_mla_amd", "csrc", "kv_layout.hip"), "rb") as fh:
+        h.update(fh.read())
+    if t.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 def load_traffic(cfg_name: str):
@@ -96,6 +116,8 @@ def main():
                     help="KV interleave size I (a divisor of the page size; the workload's own by default)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (HBM counter calibration)")
+    ap.add_argument("--op", choices=("step", "read", "relayout"), default="step",
+                    help="what to time: the decode layer-step (default) or one of the layout copies")
     ap.add_argument("--decode-only", type=int, default=0,
                     help="after the timed steps, launch the decode entry point this many more times (profiling)")
     args = ap.parse_args()
@@ -114,6 +136,8 @@ def main():
     w = configs.BY_NAME[args.config]
     if args.interleave is not None:
         w = configs.scaled(w, interleave=args.interleave, name=w.name)
+    if args.op != "step":
+        return bench_copy(args, w)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     K.load_library()
     dev = torch.device("cuda:0")
@@ -274,6 +298,135 @@ def main():
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def copy_cpu_baseline(op, w, lens, budget_s: float):
+    """The oracle's read_rows / relayout_dense timed on whole requests of the workload."""
+    import numpy as np
+    from oracle import layout as OL
+    from workloads import accounting
+    rb = accounting.kv_bytes_per_token(w) - (4 if w.kv_dtype == "fp8" else 0)
+    P, c = w.P, w.c
+    t_total, done, n = 0.0, 0, 0
+    rng = np.random.default_rng(0)
+    for b in range(w.B):
+        L = int(lens[b])
+        vp = P * c
+        nv = (L + vp - 1) // vp
+        bt = np.arange(nv, dtype=np.int32)[None, :]
+        pools = rng.integers(0, 256, size=(c, nv * P, rb), dtype=np.uint8)
+        t0 = time.perf_counter()
+        if op == "read":
+            OL.read_rows(pools, bt, [L], [0, L], P, c, w.interleave)
+        else:
+            src = rng.integers(0, 256, size=(((L + P - 1) // P) * P, rb), dtype=np.uint8)
+            sbt = np.arange((L + P - 1) // P, dtype=np.int32)[None, :]
+            OL.relayout_dense(src, sbt, [L], P, c, pools, bt, 0, c, w.interleave)
+        t_total += time.perf_counter() - t0
+        done += 2 * L * accounting.kv_bytes_per_token(w)
+        n += 1
+        if t_total >= budget_s:
+            break
+    return {"value": round(done / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"requests 0..{n - 1} of {w.name} ({n}/{w.B}), {op} of every row in a Python loop, "
+                      f"{t_total:.1f} s", "seconds": round(t_total, 2)}
+
+
+def bench_copy(args, w):
+    """Time dcp_kv_read or dcp_kv_relayout over the workload's whole context."""
+    import numpy as np
+    import torch
+
+    import kv_sharded_mla_amd as K
+    from kv_sharded_mla_amd.group import DcpGroup
+    from workloads import accounting, gen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lens = gen.lengths(w)
+    P, c = w.P, w.c
+    fp8 = w.kv_dtype == "fp8"
+    rb = accounting.kv_bytes_per_token(w) - (4 if fp8 else 0)
+    n_tok = int(lens.sum())
+    log(f"{args.op} on {w.name}: B={w.B} c={c} P={P} I={w.interleave} kv={w.kv_dtype} sum(L)={n_tok}")
+    # dense DCP1 pool with shuffled page ids, random bytes
+    rng = np.random.default_rng(17)
+    npg = [(int(L) + P - 1) // P for L in lens]
+    ids = rng.permutation(sum(npg)).astype(np.int32)
+    src_bt = np.full((w.B, max(npg)), -1, np.int32)
+    k = 0
+    for b, n in enumerate(npg):
+        src_bt[b, :n] = ids[k:k + n]
+        k += n
+    gcpu = torch.Generator(device="cuda").manual_seed(5)
+    src = torch.randint(0, 256, (sum(npg) * P * rb,), dtype=torch.uint8, device=dev, generator=gcpu)
+    ssc = torch.rand(sum(npg) * P, device=dev, generator=gcpu) if fp8 else None
+    num_pages = gen.pool_pages(w, lens)
+    vp = P * c
+    stride = int(max((int(L) + vp - 1) // vp for L in lens))
+    g = DcpGroup(c, P, num_pages, K.KV_FP8_E4M3 if fp8 else K.KV_BF16, w.B, stride,
+                 free_stack=gen.free_stack(w, num_pages), device="cuda:0", interleave=w.interleave)
+    d_lens = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    K.dcp_alloc_virtual(g.layout, g.free_stack, g.free_top, torch.zeros_like(d_lens), d_lens, g.block_table,
+                        g.dev_status)
+    d_sbt = torch.from_numpy(src_bt).to(dev)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    out = torch.empty((n_tok, rb), dtype=torch.uint8, device=dev)
+    out_sc = torch.empty(n_tok, dtype=torch.float32, device=dev) if fp8 else None
+
+    def launch():
+        if args.op == "relayout":
+            K.dcp_kv_relayout(g.layout, src, ssc, d_sbt, d_lens, 0, c, g.pools, g.pool_scales, g.block_table,
+                              g.dev_status)
+        else:
+            K.dcp_kv_read(g.layout, g.pools, g.pool_scales, g.block_table, d_lens, cu, out, out_sc, g.dev_status)
+
+    K.dcp_kv_relayout(g.layout, src, ssc, d_sbt, d_lens, 0, c, g.pools, g.pool_scales, g.block_table, g.dev_status)
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    assert g.status() == 0, g.status()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        launch()
+        e[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert g.status() == 0, g.status()
+    if args.calib_copy_mib:
+        a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        torch.empty_like(a).copy_(a)
+        torch.cuda.synchronize()
+        del a
+    t_launch = sum(a.elapsed_time(b) for a, b in evs) / args.steps       # ms
+    moved = 2 * n_tok * accounting.kv_bytes_per_token(w)                  # read + write, rows and scales
+    gbps = moved / (t_launch * 1e-3) / 1e9
+    log(f"{args.op}: {t_launch * 1e3:.1f} us per launch, {gbps:.0f} GB/s")
+    name = "dcp_kv_read (extend gather to token order)" if args.op == "read" else \
+        "dcp_kv_relayout (DCP1 paged pool -> c owner pools)"
+    out_json = {
+        "metric": f"DCP KV {args.op}: achieved HBM GB/s (bytes read + written per launch)",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic (random bytes in the " + ("e4m3 row + fp32 scale" if fp8 else "bf16 row") + " layout)",
+        "config": {"workload": w.name, "op": args.op, "batch": w.B, "dcp": c, "page": P, "interleave": w.interleave,
+                   "kv": w.kv_dtype, "context_tokens": n_tok, "emulated_ranks_on_one_gpu": c},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": load_copy_traffic(args.op, w.name),
+                     "kernel": name,
+                     "algorithmic_bytes_per_launch": moved, "launch_us": round(t_launch * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the oracle on the host for about {args.cpu_budget:.0f} s")
+        out_json["cpu_baseline"] = copy_cpu_baseline(args.op, w, lens, args.cpu_budget)
+    else:
+        out_json["cpu_baseline"] = None
+    print(json.dumps(out_json), flush=True)
 
 
 if __name__ == "__main__":

@@ -147,9 +147,13 @@ kv_write_kernel(int32_t c, int32_t il, int32_t page, int32_t num_pages, uint8_t*
 // ---- extend gather and DCP1 -> DCP c relayout -------------------------------
 // Both walk one virtual page of one request per step: rank r's P slots of
 // virtual page g (page id pg) sit contiguously in pool r at [pg*P, pg*P + P),
-// and local slot s there holds position g*P*c + (s / I)*I*c + r*I + s mod I.
+// and local slot s there holds position g*P*c + (s / I)*I*c + r*I + s mod I
+// (the gather walks the page in token order, the relayout rank by rank: the
+// stores of either are then contiguous, which measured faster than contiguous
+// loads).
 // Each wave copies whole rows (rows are wave-uniform, so the index arithmetic
-// is scalar), RPW rows per round with all loads issued before the stores.
+// is scalar), a round of four copy units at a time with all loads issued
+// before the stores.
 // Workgroup (b, k) of a batch x G grid takes virtual pages k, k + G, ... of
 // request b.
 
@@ -161,28 +165,43 @@ __device__ __forceinline__ int64_t slot_position(int64_t g, int32_t s, int32_t r
   return g * page * c + (int64_t)(s / il) * il * c + (int64_t)r * il + s % il;
 }
 
-// Lane l moves chunk l of each row and, for 72-chunk rows, lanes 0..7 also
-// chunk 64 + l; lanes past the row's chunks load an in-row chunk and store
-// nothing.
+// A copy unit is 1152 bytes: one bf16 row, or two e4m3 rows (the second
+// starting at chunk 36).  Lane l moves chunk l of each unit and lanes 0..7
+// also chunk 64 + l, so a unit takes two vector loads and two stores.
 template <bool FP8>
-__device__ __forceinline__ void copy_rows(const uint8_t* (&src)[kRowsPerWave], uint8_t* (&dst)[kRowsPerWave],
-                                          const bool (&live)[kRowsPerWave], int lane) {
-  static_assert(kRowsPerWave == 4, "four named rows below");
-  constexpr int kChunks = (FP8 ? kDqk : 2 * kDqk) / 16;   // 36 or 72 chunks of 16 bytes
-  constexpr int kTail = kChunks > 64 ? kChunks - 64 : 0;
-  const int c0 = lane < kChunks ? lane : 0;
-  const int c1 = 64 + (lane < kTail ? lane : 0);
-  // named registers rather than arrays: the loads of all four rows are in
-  // flight before the first store
+struct CopyUnits {
+  static constexpr int kRows = FP8 ? 2 * kRowsPerWave : kRowsPerWave;   // rows per wave round
+};
+
+template <bool FP8>
+__device__ __forceinline__ void copy_rows(const uint8_t* (&src)[CopyUnits<FP8>::kRows],
+                                          uint8_t* (&dst)[CopyUnits<FP8>::kRows],
+                                          const bool (&live)[CopyUnits<FP8>::kRows], int lane) {
+  static_assert(kRowsPerWave == 4, "four named units below");
+  // chunk k of unit i: row (FP8 && k >= 36 ? 2i + 1 : i * (FP8 ? 2 : 1)), chunk k mod 36 (e4m3) or k
+  auto pick = [&](int i, int k, int& row, int& ch) {
+    if (FP8) {
+      row = 2 * i + (k >= 36 ? 1 : 0);
+      ch = k >= 36 ? k - 36 : k;
+    } else {
+      row = i;
+      ch = k;
+    }
+  };
+  const int k1 = 64 + (lane < 8 ? lane : 0);
   auto ld = [&](int i, int4& x, int4& y) {
-    if (!live[i]) return;
-    x = reinterpret_cast<const int4*>(src[i])[c0];
-    if (kTail) y = reinterpret_cast<const int4*>(src[i])[c1];
+    int row, ch;
+    pick(i, lane, row, ch);
+    if (live[row]) x = reinterpret_cast<const int4*>(src[row])[ch];
+    pick(i, k1, row, ch);
+    if (lane < 8 && live[row]) y = reinterpret_cast<const int4*>(src[row])[ch];
   };
   auto st = [&](int i, const int4& x, const int4& y) {
-    if (!live[i]) return;
-    if (lane < kChunks) reinterpret_cast<int4*>(dst[i])[lane] = x;
-    if (kTail && lane < kTail) reinterpret_cast<int4*>(dst[i])[64 + lane] = y;
+    int row, ch;
+    pick(i, lane, row, ch);
+    if (live[row]) reinterpret_cast<int4*>(dst[row])[ch] = x;
+    pick(i, k1, row, ch);
+    if (lane < 8 && live[row]) reinterpret_cast<int4*>(dst[row])[ch] = y;
   };
   int4 a0 = {}, a1 = {}, a2 = {}, a3 = {}, t0 = {}, t1 = {}, t2 = {}, t3 = {};
   ld(0, a0, t0);
@@ -195,6 +214,24 @@ __device__ __forceinline__ void copy_rows(const uint8_t* (&src)[kRowsPerWave], u
   st(3, a3, t3);
 }
 
+// e4m3 scales of a round's rows: lane i moves row i's scale, one load and one
+// store for the whole round
+template <int NR>
+__device__ __forceinline__ void copy_scales(const float* __restrict__ from, float* __restrict__ to,
+                                            const int64_t (&sf)[NR], const int64_t (&stt)[NR], const bool (&live)[NR],
+                                            int lane) {
+  int64_t f = 0, t = 0;
+  bool lv = false;
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+    if (lane == i) {
+      f = sf[i];
+      t = stt[i];
+      lv = live[i];
+    }
+  if (lv) to[t] = from[f];
+}
+
 template <bool FP8>
 __global__ void __launch_bounds__(kCopyThreads)
 kv_read_kernel(int32_t c, int32_t il, int32_t page, int32_t num_pages, int32_t G, const uint8_t* __restrict__ pools,
@@ -202,6 +239,7 @@ kv_read_kernel(int32_t c, int32_t il, int32_t page, int32_t num_pages, int32_t G
                const int32_t* __restrict__ seq_len, const int32_t* __restrict__ cu_out, int64_t n_rows,
                uint8_t* __restrict__ rows_out, float* __restrict__ scales_out, int32_t* __restrict__ dev_status) {
   constexpr int64_t kRowBytes = FP8 ? kDqk : 2 * kDqk;
+  constexpr int NR = CopyUnits<FP8>::kRows;
   const int b = blockIdx.x / G, k = blockIdx.x % G;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t vpage = (int64_t)page * c;
@@ -224,21 +262,25 @@ kv_read_kernel(int32_t c, int32_t il, int32_t page, int32_t num_pages, int32_t G
       if (threadIdx.x == 0 && dev_status) atomicMax(dev_status, DCP_DEV_BAD_PAGE);
       continue;
     }
-    for (int32_t i0 = wv * kRowsPerWave; i0 < per_vp; i0 += (kCopyThreads / 64) * kRowsPerWave) {
-      const uint8_t* src[kRowsPerWave];
-      uint8_t* dst[kRowsPerWave];
-      bool live[kRowsPerWave];
+    for (int32_t i0 = wv * NR; i0 < per_vp; i0 += (kCopyThreads / 64) * NR) {
+      const uint8_t* src[NR];
+      uint8_t* dst[NR];
+      bool live[NR];
+      int64_t sc_from[NR], sc_to[NR];
 #pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i) {
-        const int32_t rl = i0 + i;
-        const int32_t r = rl / page, s = rl - r * page;
-        const int64_t pos = slot_position(g, s, r, c, il, page);
-        live[i] = rl < per_vp && pos < L;
+      for (int i = 0; i < NR; ++i) {
+        // rows in token order, so that a round's stores are contiguous
+        const int32_t o = i0 + i;
+        const int64_t pos = g * per_vp + o;
+        const int32_t r = (o / il) % c, s = (o / (il * c)) * il + o % il;
+        live[i] = o < per_vp && pos < L;
         const int64_t slot = (int64_t)pg * page + s;
         src[i] = pools + ((int64_t)r * cap + slot) * kRowBytes;
         dst[i] = out_b + pos * kRowBytes;
-        if (FP8 && live[i] && lane == 0) scales_out[cu_out[b] + pos] = pool_scales[(int64_t)r * cap + slot];
+        sc_from[i] = (int64_t)r * cap + slot;
+        sc_to[i] = cu_out[b] + pos;
       }
+      if (FP8) copy_scales<NR>(pool_scales, scales_out, sc_from, sc_to, live, lane);
       copy_rows<FP8>(src, dst, live, lane);
     }
   }
@@ -252,6 +294,7 @@ kv_relayout_kernel(int32_t c, int32_t il, int32_t page, int32_t num_pages, int32
                    const int32_t* __restrict__ seq_len, uint8_t* __restrict__ pools, float* __restrict__ pool_scales,
                    const int32_t* __restrict__ block_table, int32_t bt_stride, int32_t* __restrict__ dev_status) {
   constexpr int64_t kRowBytes = FP8 ? kDqk : 2 * kDqk;
+  constexpr int NR = CopyUnits<FP8>::kRows;
   const int b = blockIdx.x / G, k = blockIdx.x % G;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t vpage = (int64_t)page * c;
@@ -270,13 +313,14 @@ kv_relayout_kernel(int32_t c, int32_t il, int32_t page, int32_t num_pages, int32
   const int32_t per_vp = page * rank_count;   // rows of the covered ranks in one virtual page
   for (int64_t g = k; g < n_vp; g += G) {
     const int32_t pg = block_table[(int64_t)b * bt_stride + g];
-    for (int32_t i0 = wv * kRowsPerWave; i0 < per_vp; i0 += (kCopyThreads / 64) * kRowsPerWave) {
-      const uint8_t* src[kRowsPerWave];
-      uint8_t* dst[kRowsPerWave];
-      bool live[kRowsPerWave];
+    for (int32_t i0 = wv * NR; i0 < per_vp; i0 += (kCopyThreads / 64) * NR) {
+      const uint8_t* src[NR];
+      uint8_t* dst[NR];
+      bool live[NR];
+      int64_t sc_from[NR], sc_to[NR];
       int code = DCP_DEV_OK;
 #pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i) {
+      for (int i = 0; i < NR; ++i) {
         const int32_t rl = i0 + i;
         const int32_t rr = rl / page, s = rl - rr * page;
         const int32_t r = rank_begin + rr;
@@ -291,9 +335,11 @@ kv_relayout_kernel(int32_t c, int32_t il, int32_t page, int32_t num_pages, int32
         const int64_t sslot = (int64_t)sp * page + pos % page;
         src[i] = src_pool + sslot * kRowBytes;
         dst[i] = pools + ((int64_t)rr * cap + slot) * kRowBytes;
-        if (FP8 && live[i] && lane == 0) pool_scales[(int64_t)rr * cap + slot] = src_scales[sslot];
+        sc_from[i] = sslot;
+        sc_to[i] = (int64_t)rr * cap + slot;
       }
       if (code != DCP_DEV_OK && lane == 0 && dev_status) atomicMax(dev_status, code);
+      if (FP8) copy_scales<NR>(src_scales, pool_scales, sc_from, sc_to, live, lane);
       copy_rows<FP8>(src, dst, live, lane);
     }
   }
