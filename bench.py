@@ -236,6 +236,24 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     log(f"per step: wall {ms_per_step * 1e3:.1f} us; events: write {t_write * 1e3:.1f} us, decode "
         f"{t_dec * 1e3:.1f} us, merge {t_merge * 1e3:.1f} us, step {t_step * 1e3:.1f} us")
+    dec_each = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    dec_med = dec_each[len(dec_each) // 2]
+    dec_p90 = dec_each[min(len(dec_each) - 1, (9 * len(dec_each)) // 10)]
+    # one real rank's share: rank 0's pool alone (rank_begin 0, rank_count 1), as one GPU
+    # of a c-GPU group would run it
+    g = groups[0]
+    share = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for k in range(-2, len(share)):
+        if k >= 0:
+            share[k][0].record(stream)
+        K.mla_decode_partial(g.layout, g.pools, g.pool_scales, 0, 1, q, g.block_table, new_len, max_len,
+                             w.sm_scale, base, w.causal, o_part[:1], lse_part[:1], ws, g.dev_status)
+        if k >= 0:
+            share[k][1].record(stream)
+    torch.cuda.synchronize()
+    assert g.status() == 0, g.status()
+    t_share = sorted(a.elapsed_time(b) for a, b in share)[len(share) // 2]
+    log(f"decode median {dec_med * 1e3:.1f} us, p90 {dec_p90 * 1e3:.1f} us; one rank's share {t_share * 1e3:.1f} us")
     for i in range(args.decode_only):
         g = groups[i % len(groups)]
         K.mla_decode_partial(g.layout, g.pools, g.pool_scales, 0, w.c, q, g.block_table, new_len, max_len,
@@ -289,7 +307,10 @@ def main():
         "us_per_layer_step": round(ms_per_step * 1e3, 2),
         "tflops": round(tflops, 2),
         "kernel_us": {"alloc+kv_write": round(t_write * 1e3, 2), "mla_decode_partial": round(t_dec * 1e3, 2),
-                      "dcp_lse_merge": round(t_merge * 1e3, 2)},
+                      "dcp_lse_merge": round(t_merge * 1e3, 2),
+                      "mla_decode_partial_median": round(dec_med * 1e3, 2),
+                      "mla_decode_partial_p90": round(dec_p90 * 1e3, 2),
+                      "one_rank_share_decode": round(t_share * 1e3, 2)},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -29,7 +29,7 @@ class Case:
     """One workload's inputs on host and device, and its emulated group."""
 
     def __init__(self, w: Workload, lens=None, needles=None, seed_free_stack=True, sentinel=None,
-                 num_pages=None):
+                 num_pages=None, keep_rows=False):
         from kv_sharded_mla_amd import KV_BF16, KV_FP8_E4M3
         from kv_sharded_mla_amd.group import DcpGroup
         self.w = w
@@ -45,6 +45,9 @@ class Case:
                               interleave=w.interleave)
         data, scale, cu = gen.batch_rows(w, self.lens, needles=needles)
         self.cu = cu
+        # the generator's host rows, kept for the oracle when regenerating them per
+        # request would be slow (full-size workloads)
+        self.rows = (data, scale) if keep_rows else None
         rows = torch.from_numpy(data.view(np.uint8).reshape(len(data), -1)).to("cuda")
         sc = torch.from_numpy(scale).to("cuda") if scale is not None else None
         self.group.append([int(L) for L in self.lens], rows, sc)
@@ -55,6 +58,10 @@ class Case:
 
     def kv_host(self, b):
         L = int(self.lens[b])
+        if self.rows is not None:
+            data, scale = self.rows
+            a = int(self.cu[b])
+            return data[a:a + L], None if scale is None else scale[a:a + L]
         return gen.kv_rows(self.w, b, L, needles=(self.needles or {}).get(b))
 
     def run(self):
