@@ -45,12 +45,27 @@ def _pick(spec, lens, n):
     return out
 
 
+@pytest.mark.parametrize("needles", [False, True], ids=["plain", "needles"])
 @pytest.mark.parametrize("name", list(SAMPLES))
-def test_full_size_sampled(name):
+def test_full_size_sampled(name, needles):
+    """With ``needles`` the sampled requests carry a few planted keys aligned with
+    one head's query, so that some outputs are O(1) instead of near the Gaussian
+    limit sm_scale * q[:512]."""
+    from workloads import gen
     w = C.BY_NAME[name]
-    log(f"full-size {name}: B={w.B} H={w.H} q_len={w.q_len} c={w.c} kv={w.kv_dtype}")
-    case = Case(w, keep_rows=True)
+    log(f"full-size {name}{' with needles' if needles else ''}: B={w.B} H={w.H} q_len={w.q_len} c={w.c} "
+        f"kv={w.kv_dtype}")
+    lens = gen.lengths(w)
+    planted = None
+    if needles:
+        qb = gen.q_bits(w)
+        planted = {b: gen.needle_rows(w, qb, b, int(lens[b]), count=4, gain=0.6)
+                   for b in _pick(SAMPLES[name][0], lens, w.B)}
+    case = Case(w, keep_rows=True, needles=planted)
     o_part, lse_part, o, lse = case.run()
+    if needles:
+        for b in planted:
+            assert np.abs(o[b]).max() > 0.5, (b, float(np.abs(o[b]).max()))
     log(f"{name}: decoded {int(case.lens.sum())} tokens")
     for b in range(w.B):
         ro, rl = OA.merge(o_part[:, b], lse_part[:, b], w.lse_base)
