@@ -116,6 +116,8 @@ def main():
                     help="KV interleave size I (a divisor of the page size; the workload's own by default)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (HBM counter calibration)")
+    ap.add_argument("--no-share", action="store_true",
+                    help="skip timing one rank's share (profiling runs that should hold only group launches)")
     ap.add_argument("--op", choices=("step", "read", "relayout"), default="step",
                     help="what to time: the decode layer-step (default) or one of the layout copies")
     ap.add_argument("--decode-only", type=int, default=0,
@@ -243,7 +245,8 @@ def main():
     # of a c-GPU group would run it
     g = groups[0]
     share = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-    for k in range(-2, len(share)):
+    n_share = 0 if args.no_share else len(share)
+    for k in range(-2 if n_share else 0, n_share):
         if k >= 0:
             share[k][0].record(stream)
         K.mla_decode_partial(g.layout, g.pools, g.pool_scales, 0, 1, q, g.block_table, new_len, max_len,
@@ -252,8 +255,9 @@ def main():
             share[k][1].record(stream)
     torch.cuda.synchronize()
     assert g.status() == 0, g.status()
-    t_share = sorted(a.elapsed_time(b) for a, b in share)[len(share) // 2]
-    log(f"decode median {dec_med * 1e3:.1f} us, p90 {dec_p90 * 1e3:.1f} us; one rank's share {t_share * 1e3:.1f} us")
+    t_share = None if args.no_share else sorted(a.elapsed_time(b) for a, b in share)[len(share) // 2]
+    log(f"decode median {dec_med * 1e3:.1f} us, p90 {dec_p90 * 1e3:.1f} us"
+        + ("" if t_share is None else f"; one rank's share {t_share * 1e3:.1f} us"))
     for i in range(args.decode_only):
         g = groups[i % len(groups)]
         K.mla_decode_partial(g.layout, g.pools, g.pool_scales, 0, w.c, q, g.block_table, new_len, max_len,
@@ -310,7 +314,7 @@ def main():
                       "dcp_lse_merge": round(t_merge * 1e3, 2),
                       "mla_decode_partial_median": round(dec_med * 1e3, 2),
                       "mla_decode_partial_p90": round(dec_p90 * 1e3, 2),
-                      "one_rank_share_decode": round(t_share * 1e3, 2)},
+                      "one_rank_share_decode": None if t_share is None else round(t_share * 1e3, 2)},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

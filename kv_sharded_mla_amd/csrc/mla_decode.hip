@@ -48,6 +48,10 @@ constexpr int kMaxTab = 512;  // page ids staged per workgroup
 constexpr int kStageTok = 32; // tokens per LDS stage
 // score fragments in token-block-major order (each accumulator then takes its
 // MFMAs back to back) or interleaved
+// split-combine workgroups per CU (a grid-stride loop covers the rest)
+#ifndef DCP_COMBINE_BLOCKS_PER_CU
+#define DCP_COMBINE_BLOCKS_PER_CU 8
+#endif
 // work items the plan aims for per CU and row block
 #ifndef DCP_ITEMS_PER_CU
 #define DCP_ITEMS_PER_CU 2
@@ -945,7 +949,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   if (e != hipSuccess || pl.max_items == pl.units) return e;
   // at most (max_items - units) units are split; a grid-stride loop covers them
   const int64_t pairs_max = std::min<int64_t>(pl.max_items - pl.units, pl.units) * pl.rows;
-  const int64_t cgrid = std::max<int64_t>(1, std::min<int64_t>((pairs_max + 1) / 2, 2 * device_cu_count()));
+  const int64_t cgrid =
+      std::max<int64_t>(1, std::min<int64_t>((pairs_max + 1) / 2, DCP_COMBINE_BLOCKS_PER_CU * device_cu_count()));
   hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)cgrid), dim3(256), 0, stream, prm);
   return hipGetLastError();
 }
