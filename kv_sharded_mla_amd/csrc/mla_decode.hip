@@ -52,6 +52,16 @@ constexpr int kStageTok = 32; // tokens per LDS stage
 #ifndef DCP_COMBINE_BLOCKS_PER_CU
 #define DCP_COMBINE_BLOCKS_PER_CU 8
 #endif
+// one work item per CU and row block instead of two when the units are about
+// equally long
+#ifndef DCP_UNIFORM_HALVES_ITEMS
+#define DCP_UNIFORM_HALVES_ITEMS 1
+#endif
+// shortest work item in 32-token stages (shorter items pay their start-up
+// and partial write for little work)
+#ifndef DCP_ITEM_MIN_STAGES
+#define DCP_ITEM_MIN_STAGES 8
+#endif
 // work items the plan aims for per CU and row block
 #ifndef DCP_ITEMS_PER_CU
 #define DCP_ITEMS_PER_CU 2
@@ -750,12 +760,27 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     return (n + kStageTok - 1) / kStageTok;
   };
   // the first chunk's stage counts stay in a register (one read of seq_len)
+  __shared__ int32_t st_max;
   const int32_t st0 = tid < p.units ? unit_stages(tid) : 0;
   int64_t w = st0;
-  for (int32_t u = tid + 1024; u < p.units; u += 1024) w += unit_stages(u);
+  int32_t mx = st0;
+  for (int32_t u = tid + 1024; u < p.units; u += 1024) {
+    const int32_t st = unit_stages(u);
+    w += st;
+    mx = st > mx ? st : mx;
+  }
+  if (tid == 0) st_max = 0;
+  __syncthreads();
+  atomicMax(&st_max, mx);
   int64_t W;
-  block_excl_scan(w, wtot, W);
-  int64_t T = (W + p.items_target - 1) / p.items_target;
+  block_excl_scan(w, wtot, W);   // its barriers also publish st_max
+  // When the units are about equally long (the longest at most 1.25 x the
+  // mean) there is no ragged tail to spread, and one item per CU and row
+  // block beats two: each item pays a q load, a pipeline fill and, when its
+  // unit is split, a partial write and its share of the combine.
+  int64_t target = p.items_target;
+  if (DCP_UNIFORM_HALVES_ITEMS && (int64_t)st_max * p.units * 4 <= W * 5) target = target > 1 ? target / 2 : 1;
+  int64_t T = (W + target - 1) / target;
   T = T < p.t_min ? p.t_min : (T > p.t_max ? p.t_max : T);
   auto plan_of = [&](int32_t st, int32_t& items, int32_t& len) {
     if (st == 0) {
@@ -815,25 +840,98 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   }
 }
 
+// Merge of the base-2 partials [0, n) of one row over columns 8t..8t+7, all
+// weighted against their own maximum: acc = sum_r 2^(l_r - m) o_r / tot and
+// lse = m + log2 tot; no partial (or only empty ones): lse = -inf, acc = 0.
+// The partials are loaded 8 at a time before they are combined.
+__device__ __forceinline__ void merge_cols8(const float* __restrict__ o, int64_t o_stride,
+                                            const float* __restrict__ lse, int64_t lse_stride, int n, int t,
+                                            f32x4& a0, f32x4& a1, float& lse_out) {
+  float m = -INFINITY;
+  for (int r = 0; r < n; ++r) m = fmaxf(m, lse[r * lse_stride]);
+  a0 = f32x4{0.f, 0.f, 0.f, 0.f};
+  a1 = a0;
+  lse_out = -INFINITY;
+  if (m == -INFINITY) return;
+  float tot = 0.f;
+  for (int r0 = 0; r0 < n; r0 += 8) {
+    float l[8];
+    f32x4 v0[8], v1[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (r0 + k < n) {
+        l[k] = lse[(r0 + k) * lse_stride];
+        v0[k] = *reinterpret_cast<const f32x4*>(o + (r0 + k) * o_stride + 8 * t);
+        v1[k] = *reinterpret_cast<const f32x4*>(o + (r0 + k) * o_stride + 8 * t + 4);
+      }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (r0 + k < n && l[k] != -INFINITY) {
+        const float w = exp2f(l[k] - m);
+        tot += w;
+        a0 += w * v0[k];
+        a1 += w * v1[k];
+      }
+  }
+  const float inv = 1.0f / tot;
+  a0 *= inv;
+  a1 *= inv;
+  lse_out = m + log2f(tot);
+}
+
 // Merge the items of every split unit, row by row: partials (lse in base 2)
 // -> o_part, lse_part in the requested base.  Units with one item were
-// written directly by the decode kernel.  Two rows per 256-thread block,
-// grid-stride over (split unit, row) pairs.
+// written directly by the decode kernel.  One (split unit, row) pair per
+// 256-thread workgroup at a time, grid-stride: each of the four 64-thread
+// groups merges a quarter of the unit's items (8 columns per thread), and
+// the first group merges the four results (the same log-sum-exp merge, so
+// long runs of items are not one serial chain of loads).
 __global__ void __launch_bounds__(256) split_combine_kernel(DecodeParams p) {
+  __shared__ float s_lse[4];
+  __shared__ f32x4 s_acc[4][64][2];
+  const int grp = threadIdx.x >> 6, t = threadIdx.x & 63;
   const int64_t n_pairs = (int64_t)p.n_items[1] * p.rows;
-  const int col4 = threadIdx.x & 127;
-  for (int64_t pr = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7); pr < n_pairs; pr += (int64_t)gridDim.x * 2) {
+  for (int64_t pr = blockIdx.x; pr < n_pairs; pr += gridDim.x) {
     const int32_t unit = p.split_units[pr / p.rows];
     const int rr = (int)(pr % p.rows);
     const int64_t first = p.unit_first[unit];
     const int32_t cnt = p.unit_count[unit];
-    f32x4 acc;
-    float lse2;
-    merge_row4(p.ws_o + (first * p.rows + rr) * kDv, (int64_t)p.rows * kDv, p.ws_lse + first * p.rows + rr, p.rows,
-               cnt, true, col4, acc, lse2);
-    const int64_t row = (int64_t)unit * p.rows + rr;
-    *reinterpret_cast<f32x4*>(p.o_part + row * kDv + 4 * col4) = acc;
-    if (col4 == 0) p.lse_part[row] = p.out_base2 ? lse2 : lse2 * kLn2;
+    const int32_t a = (int32_t)((int64_t)cnt * grp / 4), b = (int32_t)((int64_t)cnt * (grp + 1) / 4);
+    f32x4 a0, a1;
+    float l2;
+    merge_cols8(p.ws_o + ((first + a) * p.rows + rr) * kDv, (int64_t)p.rows * kDv, p.ws_lse + (first + a) * p.rows + rr,
+                p.rows, b - a, t, a0, a1, l2);
+    s_acc[grp][t][0] = a0;
+    s_acc[grp][t][1] = a1;
+    if (t == 0) s_lse[grp] = l2;
+    __syncthreads();
+    if (grp == 0) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = fmaxf(m, s_lse[k]);
+      f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+      float lse2 = -INFINITY;
+      if (m != -INFINITY) {
+        float tot = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (s_lse[k] != -INFINITY) {
+            const float w = exp2f(s_lse[k] - m);
+            tot += w;
+            o0 += w * s_acc[k][t][0];
+            o1 += w * s_acc[k][t][1];
+          }
+        const float inv = 1.0f / tot;
+        o0 *= inv;
+        o1 *= inv;
+        lse2 = m + log2f(tot);
+      }
+      const int64_t row = (int64_t)unit * p.rows + rr;
+      *reinterpret_cast<f32x4*>(p.o_part + row * kDv + 8 * t) = o0;
+      *reinterpret_cast<f32x4*>(p.o_part + row * kDv + 8 * t + 4) = o1;
+      if (t == 0) p.lse_part[row] = p.out_base2 ? lse2 : lse2 * kLn2;
+    }
+    __syncthreads();
   }
 }
 
@@ -877,7 +975,7 @@ DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, in
   const int64_t n_r_max = (max_seq_len + cyc - 1) / cyc * interleave;
   const int64_t stages_max = (n_r_max + kStageTok - 1) / kStageTok;
   pl.t_max = (int32_t)std::max<int64_t>(1, (int64_t)(kMaxTab - 1) * page / kStageTok);
-  pl.t_min = std::min<int32_t>(8, pl.t_max);
+  pl.t_min = std::min<int32_t>(DCP_ITEM_MIN_STAGES, pl.t_max);
   pl.items_target = std::max<int32_t>(1, DCP_ITEMS_PER_CU * device_cu_count() / pl.n_row_blocks);
   // the device plan makes at most units + max(items_target, units * ceil(stages_max / t_max)) items
   pl.max_items = pl.units + std::max<int64_t>(pl.items_target, pl.units * ((stages_max + pl.t_max - 1) / pl.t_max));
@@ -950,7 +1048,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   // at most (max_items - units) units are split; a grid-stride loop covers them
   const int64_t pairs_max = std::min<int64_t>(pl.max_items - pl.units, pl.units) * pl.rows;
   const int64_t cgrid =
-      std::max<int64_t>(1, std::min<int64_t>((pairs_max + 1) / 2, DCP_COMBINE_BLOCKS_PER_CU * device_cu_count()));
+      std::max<int64_t>(1, std::min<int64_t>(pairs_max, DCP_COMBINE_BLOCKS_PER_CU * device_cu_count()));
   hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)cgrid), dim3(256), 0, stream, prm);
   return hipGetLastError();
 }
