@@ -4,8 +4,11 @@ Small cases span several LDS stages, ragged tails, empty shards (L < c),
 zero-length requests, every row-block shape (16/32/64 rows per workgroup and
 several blocks), q_len 4 causal verification, non-causal multi-row queries,
 base-2 LSE, pages that do not align with a stage, KV splits with their
-combine, the e4m3 format, and interleave sizes I > 1 (runs of I positions
-per owner, including runs that leave whole ranks empty).  Each compares every request's merged output
+combine, the e4m3 format, interleave sizes I > 1 (runs of I positions
+per owner, including runs that leave whole ranks empty), and the limits:
+q_len 8, 256 heads, 16 owner pools, 256-token pages, and verification rows
+whose causal limit falls before position 0 (they see nothing: lse = -inf,
+o = 0, on every rank and after the merge).  Each compares every request's merged output
 and every rank's partial with the oracle at the stated tolerances.
 """
 import numpy as np
@@ -45,6 +48,13 @@ CASES = [
     ("fp8_splits", W(index=68, H=64, c=1, P=64, fixed_len=40000, kv_dtype="fp8"), None),
     ("fp8_one_to_four_stages", W(index=72, H=32, c=1, P=64, B=5, kv_dtype="fp8"), [1, 40, 70, 100, 128]),
     ("fp8_empty_shards", W(index=73, H=64, c=8, P=16, fixed_len=5, kv_dtype="fp8"), None),
+    # the largest verification step (q_len 8), many heads, a wide group, large pages
+    ("verify_q8_h32", W(index=91, H=32, q_len=8, c=4, P=64, fixed_len=1000, B=2), None),
+    ("fp8_verify_q8_h16", W(index=92, H=16, q_len=8, c=2, P=32, fixed_len=333, kv_dtype="fp8"), None),
+    ("h256_q1", W(index=93, H=256, c=2, P=64, fixed_len=900), None),
+    ("c16_wide_group", W(index=94, H=16, c=16, P=16, fixed_len=1500, B=2), None),
+    ("page_256", W(index=95, H=64, c=4, P=256, fixed_len=3000), None),
+    ("verify_q8_shorter_than_q_len", W(index=96, H=16, q_len=8, c=4, P=16, B=3), [1, 5, 8]),
     # interleave size I > 1: owners take runs of I consecutive positions
     ("il16_h64", W(index=80, H=64, c=4, P=64, fixed_len=777, interleave=16), None),
     ("il64_two_owners_of_eight", W(index=81, H=32, c=8, P=64, fixed_len=100, interleave=64), None),
