@@ -120,3 +120,33 @@ def test_workspace_size_covers_the_work_plan(lib):
         assert mla_decode_workspace_size(_layout(8, 64, 100, 0, 64), 8, 64, 1, 16, L) >= \
             mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 64, 1, 16, L)
     assert mla_decode_workspace_size(_layout(8, 64, 100, 0, 48), 8, 64, 1, 16, 1000) == 0
+
+
+def test_layout_copy_argument_errors(lib):
+    """dcp_kv_read / dcp_kv_relayout reject bad arguments on the host (nothing enqueued)."""
+    L = _layout()
+    ref = ctypes.byref(L)
+
+    def read(**kw):
+        a = dict(pools=16, ps=None, bt=16, bts=4, sl=16, cu=16, B=2, n=8, out=16, osc=None, st=None, stream=None)
+        a.update(kw)
+        return lib.dcp_kv_read(ref if "lay" not in kw else kw["lay"], a["pools"], a["ps"], a["bt"], a["bts"], a["sl"],
+                               a["cu"], a["B"], a["n"], a["out"], a["osc"], a["st"], a["stream"])
+    assert read(B=0) == 0                      # nothing to do
+    assert read(B=-1) == -1 and read(B=65537) == -1 and read(n=-1) == -1 and read(bts=0) == -1
+    assert read(pools=None) == -1 and read(cu=None) == -1 and read(out=None) == -1
+    assert read(out=8) == -3                   # rows_out not 16-byte aligned
+    assert read(lay=ctypes.byref(_layout(kv=1))) == -1          # e4m3 needs the scale arrays
+    assert read(lay=ctypes.byref(_layout(c=1 << 16, page=1 << 15, num_pages=1))) == -2   # page * c > 2^30
+
+    def relayout(**kw):
+        a = dict(src=16, ssc=None, snp=4, sbt=16, sbts=4, sl=16, B=2, rb=0, rc=4, pools=16, ps=None, bt=16, bts=4,
+                 st=None, stream=None)
+        a.update(kw)
+        return lib.dcp_kv_relayout(ref, a["src"], a["ssc"], a["snp"], a["sbt"], a["sbts"], a["sl"], a["B"], a["rb"],
+                                   a["rc"], a["pools"], a["ps"], a["bt"], a["bts"], a["st"], a["stream"])
+    assert relayout(B=0) == 0
+    assert relayout(rb=-1) == -1 and relayout(rc=0) == -1 and relayout(rb=2, rc=3) == -1   # ranks within [0, c)
+    assert relayout(snp=-1) == -1 and relayout(sbts=0) == -1 and relayout(bts=0) == -1
+    assert relayout(src=None) == -1 and relayout(sbt=None) == -1 and relayout(pools=None) == -1
+    assert relayout(src=8) == -3 and relayout(pools=24) == -3
