@@ -8,7 +8,8 @@ combine, the e4m3 format, interleave sizes I > 1 (runs of I positions
 per owner, including runs that leave whole ranks empty), and the limits:
 q_len 8, 256 heads, 16 owner pools, 256-token pages, and verification rows
 whose causal limit falls before position 0 (they see nothing: lse = -inf,
-o = 0, on every rank and after the merge).  Each compares every request's merged output
+o = 0, on every rank and after the merge); a zero and a negative softmax
+scale; e4m3 with base-2 LSE.  Each compares every request's merged output
 and every rank's partial with the oracle at the stated tolerances.
 """
 import numpy as np
@@ -55,6 +56,11 @@ CASES = [
     ("c16_wide_group", W(index=94, H=16, c=16, P=16, fixed_len=1500, B=2), None),
     ("page_256", W(index=95, H=64, c=4, P=256, fixed_len=3000), None),
     ("verify_q8_shorter_than_q_len", W(index=96, H=16, q_len=8, c=4, P=16, B=3), [1, 5, 8]),
+    # degenerate scales: a zero scale gives uniform weights (o = mean of the
+    # visible V rows, lse = ln n), a negative one favours the lowest scores
+    ("zero_scale", W(index=97, H=32, q_len=2, c=4, P=16, fixed_len=500, sm_scale=0.0), None),
+    ("negative_scale", W(index=98, H=16, c=3, P=32, fixed_len=400, sm_scale=-C.SM_SCALE), None),
+    ("fp8_base2", W(index=99, H=64, c=4, P=64, fixed_len=2000, kv_dtype="fp8", lse_base="2"), None),
     # interleave size I > 1: owners take runs of I consecutive positions
     ("il16_h64", W(index=80, H=64, c=4, P=64, fixed_len=777, interleave=16), None),
     ("il64_two_owners_of_eight", W(index=81, H=32, c=8, P=64, fixed_len=100, interleave=64), None),
