@@ -168,11 +168,15 @@ def test_kv_relayout_errors_skip_and_report():
         assert np.array_equal(d_pools.cpu().numpy().reshape(c, 2 * P, 1152), want)
 
 
-def test_relayout_then_read_round_trip_full_size():
-    """16-head workload shape: 64 requests of 32768 tokens, c = 8, P = 64, bf16 rows."""
+@pytest.mark.parametrize("name", ["tplocal", "long"])
+def test_relayout_then_read_round_trip_full_size(name):
+    """Full workload shapes: 64 requests of 32768 tokens (c = 8, P = 64, bf16 rows) and 4
+    requests of 1,048,576 tokens (c = 8, P = 64, e4m3 rows with their scales)."""
     K = _lib()
     from workloads import configs as C, gen
-    w = C.BY_NAME["tplocal"]
+    w = C.BY_NAME[name]
+    fp8 = w.kv_dtype == "fp8"
+    rb = 576 if fp8 else 1152
     lens = gen.lengths(w)
     B, P, c = w.B, w.P, w.c
     rng = np.random.default_rng(11)
@@ -186,21 +190,24 @@ def test_relayout_then_read_round_trip_full_size():
         src_bt[b, :n] = ids[k:k + n]
         k += n
     g = torch.Generator(device="cuda").manual_seed(3)
-    src = torch.randint(0, 256, (src_pages * P, 1152), dtype=torch.uint8, device="cuda", generator=g)
+    src = torch.randint(0, 256, (src_pages * P, rb), dtype=torch.uint8, device="cuda", generator=g)
+    ssc = torch.rand(src_pages * P, device="cuda", generator=g) if fp8 else None
     num_pages = gen.pool_pages(w, lens)
     vp = P * c
     stride = int(max((int(L) + vp - 1) // vp for L in lens))
     st, _, bt = OL.alloc_virtual(gen.free_stack(w, num_pages), num_pages, np.zeros(B, np.int64), lens,
                                  np.full((B, stride), -1, np.int32), P, c)
     assert st == OL.OK
-    layout = K.make_layout(c, P, num_pages, K.KV_BF16)
-    pools = torch.zeros(c * num_pages * P * 1152, dtype=torch.uint8, device="cuda")
+    layout = K.make_layout(c, P, num_pages, K.KV_FP8_E4M3 if fp8 else K.KV_BF16)
+    pools = torch.zeros(c * num_pages * P * rb, dtype=torch.uint8, device="cuda")
+    pscales = torch.zeros(c * num_pages * P, dtype=torch.float32, device="cuda") if fp8 else None
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     d_bt, d_lens = _t(bt), _t(lens)
-    K.dcp_kv_relayout(layout, src, None, _t(src_bt), d_lens, 0, c, pools, None, d_bt, status)
+    K.dcp_kv_relayout(layout, src, ssc, _t(src_bt), d_lens, 0, c, pools, pscales, d_bt, status)
     cu = np.concatenate([[0], np.cumsum(lens)])
-    out = torch.empty((int(cu[-1]), 1152), dtype=torch.uint8, device="cuda")
-    K.dcp_kv_read(layout, pools, None, d_bt, d_lens, _t(cu), out, None, status)
+    out = torch.empty((int(cu[-1]), rb), dtype=torch.uint8, device="cuda")
+    out_sc = torch.empty(int(cu[-1]), dtype=torch.float32, device="cuda") if fp8 else None
+    K.dcp_kv_read(layout, pools, pscales, d_bt, d_lens, _t(cu), out, out_sc, status)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     # token order of the dense pool: row p of request b is at src_bt[b][p // P] * P + p % P
@@ -208,11 +215,16 @@ def test_relayout_then_read_round_trip_full_size():
     req = np.repeat(np.arange(B), lens)
     idx = torch.from_numpy(src_bt[req, pos // P].astype(np.int64) * P + pos % P).cuda()
     assert torch.equal(out, src.index_select(0, idx))
+    if fp8:
+        assert torch.equal(out_sc.view(torch.int32), ssc.index_select(0, idx).view(torch.int32))
     # sampled positions against the oracle's slot map, straight from the striped pools
-    pv = pools.view(c, num_pages * P, 1152)
+    pv = pools.view(c, num_pages * P, rb)
     for _ in range(256):
         b = int(rng.integers(0, B))
         p = int(rng.integers(0, int(lens[b])))
         r, s = OL.slot_of(bt[b], p, P, c)
-        assert torch.equal(pv[r, s], src[int(src_bt[b, p // P]) * P + p % P])
-    log(f"relayout + read round trip: {int(cu[-1])} rows of 1152 B ok")
+        srow = int(src_bt[b, p // P]) * P + p % P
+        assert torch.equal(pv[r, s], src[srow])
+        if fp8:
+            assert float(pscales[r * num_pages * P + s]) == float(ssc[srow])
+    log(f"{name}: relayout + read round trip of {int(cu[-1])} rows of {rb} B ok")
