@@ -72,6 +72,28 @@ def load_traffic(cfg_name: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def host_info():
+    """CPU model and BLAS library the oracle runs on (for the baseline's record)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        pass
+    return model, blas
+
+
 def cpu_baseline(w, lens, budget_s: float):
     """The oracle as it stands (rank partials + merge), timed on a sample of requests."""
     import numpy as np
@@ -100,7 +122,7 @@ def cpu_baseline(w, lens, budget_s: float):
     return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"requests 0..{n - 1} of {w.name} ({n}/{w.B}), all {w.H} heads x q_len {w.q_len}, "
                       f"{w.c} rank partials + merge in float64, {t_total:.1f} s",
-            "seconds": round(t_total, 2)}
+            "seconds": round(t_total, 2), "cpu_model": host_info()[0], "blas": host_info()[1]}
 
 
 def main():
