@@ -57,6 +57,10 @@ constexpr int kStageTok = 32; // tokens per LDS stage
 #ifndef DCP_UNIFORM_HALVES_ITEMS
 #define DCP_UNIFORM_HALVES_ITEMS 1
 #endif
+// list the single-item units of a ragged batch longest first
+#ifndef DCP_SORT_SINGLE_ITEMS
+#define DCP_SORT_SINGLE_ITEMS 1
+#endif
 // shortest work item in 32-token stages (shorter items pay their start-up
 // and partial write for little work)
 #ifndef DCP_ITEM_MIN_STAGES
@@ -779,7 +783,8 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   // block beats two: each item pays a q load, a pipeline fill and, when its
   // unit is split, a partial write and its share of the combine.
   int64_t target = p.items_target;
-  if (DCP_UNIFORM_HALVES_ITEMS && (int64_t)st_max * p.units * 4 <= W * 5) target = target > 1 ? target / 2 : 1;
+  const bool uniform = (int64_t)st_max * p.units * 4 <= W * 5;
+  if (DCP_UNIFORM_HALVES_ITEMS && uniform) target = target > 1 ? target / 2 : 1;
   int64_t T = (W + target - 1) / target;
   T = T < p.t_min ? p.t_min : (T > p.t_max ? p.t_max : T);
   auto plan_of = [&](int32_t st, int32_t& items, int32_t& len) {
@@ -806,6 +811,25 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
       multi_total += tot;
     }
   }
+  // With ragged lengths (and at most 1024 units) the single-item units are
+  // listed longest first, so that the longest work starts first and the
+  // short units fill the tail: a unit's rank counts the single units that
+  // are longer, or as long with a lower index.
+  __shared__ int32_t s_key[1024];
+  const bool sort_singles = DCP_SORT_SINGLE_ITEMS && !uniform && p.units <= 1024;
+  int32_t single_rank = 0;
+  if (sort_singles) {
+    int32_t items = 0, len = 0;
+    if (tid < p.units) plan_of(st0, items, len);
+    const int32_t key = (tid < p.units && items == 1) ? st0 : -1;
+    s_key[tid] = key;
+    __syncthreads();
+    if (key >= 0)
+      for (int32_t k = 0; k < p.units; ++k) {
+        const int32_t o = s_key[k];
+        single_rank += (o > key) || (o == key && k < tid);
+      }
+  }
   // item offsets: items of split units in the high 32 bits, single-item
   // units in the low 32 bits; a second scan numbers the split units
   int64_t carry = 0, carry_split = 0;
@@ -821,7 +845,8 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     const int64_t nsplit = carry_split + block_excl_scan(items > 1 ? 1 : 0, wtot, tot_split);
     if (p.units <= 1024) multi_total = tot >> 32;
     if (u < p.units) {
-      const int32_t first = items > 1 ? (int32_t)(off >> 32) : (int32_t)(multi_total + (off & 0xffffffffLL));
+      int32_t first = items > 1 ? (int32_t)(off >> 32) : (int32_t)(multi_total + (off & 0xffffffffLL));
+      if (sort_singles && items == 1) first = (int32_t)multi_total + single_rank;
       p.unit_first[u] = first;
       p.unit_count[u] = items;
       for (int32_t k = 0; k < items; ++k) {
