@@ -103,7 +103,7 @@ struct DecodeParams {
   int32_t max_items;
   int32_t items_target;  // work items per row block the plan aims for
   int32_t t_min, t_max;  // bounds of an item's length in stages
-  int32_t* n_items;      // [2]: work items, split units
+  int32_t* n_items;      // [3]: work items, split units, most items of one unit
   int32_t* item_unit;    // [max_items]
   int32_t* item_jb;      // [max_items] first rank-local token of the item
   int32_t* item_je;      // [max_items] end of the item's tokens
@@ -862,6 +862,9 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   if (tid == 0) {
     p.n_items[0] = (int32_t)(multi_total + (carry & 0xffffffffLL));
     p.n_items[1] = (int32_t)carry_split;
+    int32_t items_max = 0, len = 0;
+    plan_of(st_max, items_max, len);
+    p.n_items[2] = items_max;
   }
 }
 
@@ -906,16 +909,35 @@ __device__ __forceinline__ void merge_cols8(const float* __restrict__ o, int64_t
 
 // Merge the items of every split unit, row by row: partials (lse in base 2)
 // -> o_part, lse_part in the requested base.  Units with one item were
-// written directly by the decode kernel.  One (split unit, row) pair per
-// 256-thread workgroup at a time, grid-stride: each of the four 64-thread
-// groups merges a quarter of the unit's items (8 columns per thread), and
-// the first group merges the four results (the same log-sum-exp merge, so
-// long runs of items are not one serial chain of loads).
+// written directly by the decode kernel.  With fewer than 8 items in every
+// unit, each 64-thread group of a 256-thread workgroup merges one (split
+// unit, row) pair (8 columns per thread), grid-stride.  Otherwise a
+// workgroup takes one pair at a time: each of its four groups merges a
+// quarter of the unit's items and the first group merges the four results
+// (the same log-sum-exp merge, so long runs of items are not one serial
+// chain of loads).
 __global__ void __launch_bounds__(256) split_combine_kernel(DecodeParams p) {
   __shared__ float s_lse[4];
   __shared__ f32x4 s_acc[4][64][2];
   const int grp = threadIdx.x >> 6, t = threadIdx.x & 63;
   const int64_t n_pairs = (int64_t)p.n_items[1] * p.rows;
+  if (p.n_items[2] < 8) {
+    // few items per unit: each 64-thread group merges a pair of its own
+    for (int64_t pr = (int64_t)blockIdx.x * 4 + grp; pr < n_pairs; pr += (int64_t)gridDim.x * 4) {
+      const int32_t unit = p.split_units[pr / p.rows];
+      const int rr = (int)(pr % p.rows);
+      const int64_t first = p.unit_first[unit];
+      f32x4 o0, o1;
+      float l2;
+      merge_cols8(p.ws_o + (first * p.rows + rr) * kDv, (int64_t)p.rows * kDv, p.ws_lse + first * p.rows + rr,
+                  p.rows, p.unit_count[unit], t, o0, o1, l2);
+      const int64_t row = (int64_t)unit * p.rows + rr;
+      *reinterpret_cast<f32x4*>(p.o_part + row * kDv + 8 * t) = o0;
+      *reinterpret_cast<f32x4*>(p.o_part + row * kDv + 8 * t + 4) = o1;
+      if (t == 0) p.lse_part[row] = p.out_base2 ? l2 : l2 * kLn2;
+    }
+    return;
+  }
   for (int64_t pr = blockIdx.x; pr < n_pairs; pr += gridDim.x) {
     const int32_t unit = p.split_units[pr / p.rows];
     const int rr = (int)(pr % p.rows);
@@ -1007,7 +1029,7 @@ DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, in
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   pl.off_ws_lse = al((size_t)pl.max_items * pl.rows * kDv * sizeof(float));
   pl.off_ints = pl.off_ws_lse + al((size_t)pl.max_items * pl.rows * sizeof(float));
-  pl.workspace_bytes = pl.off_ints + al((size_t)(2 + 3 * pl.max_items + 3 * pl.units) * sizeof(int32_t));
+  pl.workspace_bytes = pl.off_ints + al((size_t)(3 + 3 * pl.max_items + 3 * pl.units) * sizeof(int32_t));
   return pl;
 }
 
@@ -1050,7 +1072,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   prm.ws_lse = (float*)(ws + pl.off_ws_lse);
   int32_t* ints = (int32_t*)(ws + pl.off_ints);
   prm.n_items = ints;
-  prm.item_unit = ints + 2;
+  prm.item_unit = ints + 3;
   prm.item_jb = prm.item_unit + pl.max_items;
   prm.item_je = prm.item_jb + pl.max_items;
   prm.unit_first = prm.item_je + pl.max_items;
