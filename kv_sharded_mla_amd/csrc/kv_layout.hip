@@ -173,6 +173,14 @@ struct CopyUnits {
   static constexpr int kRows = FP8 ? 2 * kRowsPerWave : kRowsPerWave;   // rows per wave round
 };
 
+// Stores carry the non-temporal hint (the copied rows are not read back by
+// this kernel): 1-2% faster on every measured workload than plain stores;
+// the same hint on the loads gained nothing.
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void stv(int4* p, int4 v) {
+  __builtin_nontemporal_store(v4i{v.x, v.y, v.z, v.w}, reinterpret_cast<v4i*>(p));
+}
+
 template <bool FP8>
 __device__ __forceinline__ void copy_rows(const uint8_t* (&src)[CopyUnits<FP8>::kRows],
                                           uint8_t* (&dst)[CopyUnits<FP8>::kRows],
@@ -199,9 +207,9 @@ __device__ __forceinline__ void copy_rows(const uint8_t* (&src)[CopyUnits<FP8>::
   auto st = [&](int i, const int4& x, const int4& y) {
     int row, ch;
     pick(i, lane, row, ch);
-    if (live[row]) reinterpret_cast<int4*>(dst[row])[ch] = x;
+    if (live[row]) stv(reinterpret_cast<int4*>(dst[row]) + ch, x);
     pick(i, k1, row, ch);
-    if (lane < 8 && live[row]) reinterpret_cast<int4*>(dst[row])[ch] = y;
+    if (lane < 8 && live[row]) stv(reinterpret_cast<int4*>(dst[row]) + ch, y);
   };
   int4 a0 = {}, a1 = {}, a2 = {}, a3 = {}, t0 = {}, t1 = {}, t2 = {}, t3 = {};
   ld(0, a0, t0);

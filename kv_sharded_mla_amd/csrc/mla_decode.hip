@@ -754,8 +754,70 @@ __device__ __forceinline__ int64_t block_excl_scan(int64_t v, int64_t* wtot, int
   return before + x - v;
 }
 
+// Two exclusive prefix sums over the 1024 threads at once (one pair of
+// barriers for both).
+__device__ __forceinline__ void block_excl_scan2(int64_t va, int64_t vb, int64_t* wtot, int64_t& pa, int64_t& pb,
+                                                 int64_t& ta, int64_t& tb) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int64_t a = va, b = vb;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t ya = __shfl_up(a, o), yb = __shfl_up(b, o);
+    if (lane >= o) {
+      a += ya;
+      b += yb;
+    }
+  }
+  if (lane == 63) {
+    wtot[wv] = a;
+    wtot[16 + wv] = b;
+  }
+  __syncthreads();
+  int64_t ba = 0, bb = 0;
+  ta = 0;
+  tb = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t x = wtot[i], y = wtot[16 + i];
+    if (i < wv) {
+      ba += x;
+      bb += y;
+    }
+    ta += x;
+    tb += y;
+  }
+  __syncthreads();
+  pa = ba + a - va;
+  pb = bb + b - vb;
+}
+
+// Sum and maximum over the 1024 threads of a workgroup (every thread gets both).
+__device__ __forceinline__ void block_sum_max(int64_t v, int32_t m, int64_t* wtot, int64_t& sum, int32_t& mx) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    v += __shfl_xor(v, o);
+    const int32_t y = __shfl_xor(m, o);
+    m = y > m ? y : m;
+  }
+  if (lane == 0) {
+    wtot[wv] = v;
+    wtot[16 + wv] = m;
+  }
+  __syncthreads();
+  sum = 0;
+  mx = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sum += wtot[i];
+    const int32_t y = (int32_t)wtot[16 + i];
+    mx = y > mx ? y : mx;
+  }
+  __syncthreads();
+}
+
 __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
-  __shared__ int64_t wtot[16];
+  __shared__ int64_t wtot[32];
   const int tid = threadIdx.x;
   auto unit_stages = [&](int32_t u) -> int32_t {
     const int b = u % p.batch, rl = u / p.batch;
@@ -764,7 +826,6 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     return (n + kStageTok - 1) / kStageTok;
   };
   // the first chunk's stage counts stay in a register (one read of seq_len)
-  __shared__ int32_t st_max;
   const int32_t st0 = tid < p.units ? unit_stages(tid) : 0;
   int64_t w = st0;
   int32_t mx = st0;
@@ -773,11 +834,9 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     w += st;
     mx = st > mx ? st : mx;
   }
-  if (tid == 0) st_max = 0;
-  __syncthreads();
-  atomicMax(&st_max, mx);
   int64_t W;
-  block_excl_scan(w, wtot, W);   // its barriers also publish st_max
+  int32_t st_max;
+  block_sum_max(w, mx, wtot, W, st_max);
   // When the units are about equally long (the longest at most 1.25 x the
   // mean) there is no ragged tail to spread, and one item per CU and row
   // block beats two: each item pays a q load, a pipeline fill and, when its
@@ -815,7 +874,7 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   // listed longest first, so that the longest work starts first and the
   // short units fill the tail: a unit's rank counts the single units that
   // are longer, or as long with a lower index.
-  __shared__ int32_t s_key[1024];
+  __shared__ __attribute__((aligned(16))) int32_t s_key[1024];
   const bool sort_singles = DCP_SORT_SINGLE_ITEMS && !uniform && p.units <= 1024;
   int32_t single_rank = 0;
   if (sort_singles) {
@@ -824,11 +883,18 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     const int32_t key = (tid < p.units && items == 1) ? st0 : -1;
     s_key[tid] = key;
     __syncthreads();
-    if (key >= 0)
-      for (int32_t k = 0; k < p.units; ++k) {
-        const int32_t o = s_key[k];
-        single_rank += (o > key) || (o == key && k < tid);
+    if (key >= 0) {
+      // keys past the last unit are -1 and never count; four keys per read
+      const int32_t n4 = (p.units + 3) >> 2;
+      for (int32_t k4 = 0; k4 < n4; ++k4) {
+        const int4 o = *reinterpret_cast<const int4*>(&s_key[4 * k4]);
+        const int32_t k = 4 * k4;
+        single_rank += (o.x > key) || (o.x == key && k < tid);
+        single_rank += (o.y > key) || (o.y == key && k + 1 < tid);
+        single_rank += (o.z > key) || (o.z == key && k + 2 < tid);
+        single_rank += (o.w > key) || (o.w == key && k + 3 < tid);
       }
+    }
   }
   // item offsets: items of split units in the high 32 bits, single-item
   // units in the low 32 bits; a second scan numbers the split units
@@ -840,9 +906,11 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
       st = base == 0 ? st0 : unit_stages(u);
       plan_of(st, items, len);
     }
-    int64_t tot, tot_split;
-    const int64_t off = carry + block_excl_scan(items > 1 ? ((int64_t)items << 32) : (int64_t)items, wtot, tot);
-    const int64_t nsplit = carry_split + block_excl_scan(items > 1 ? 1 : 0, wtot, tot_split);
+    int64_t tot, tot_split, off, nsplit;
+    block_excl_scan2(items > 1 ? ((int64_t)items << 32) : (int64_t)items, items > 1 ? 1 : 0, wtot, off, nsplit, tot,
+                     tot_split);
+    off += carry;
+    nsplit += carry_split;
     if (p.units <= 1024) multi_total = tot >> 32;
     if (u < p.units) {
       int32_t first = items > 1 ? (int32_t)(off >> 32) : (int32_t)(multi_total + (off & 0xffffffffLL));
