@@ -6,7 +6,8 @@ several blocks), q_len 4 causal verification, non-causal multi-row queries,
 base-2 LSE, pages that do not align with a stage, KV splits with their
 combine, the e4m3 format, interleave sizes I > 1 (runs of I positions
 per owner, including runs that leave whole ranks empty), and the limits:
-q_len 8, 256 heads, 16 owner pools, 256-token pages, and verification rows
+q_len 8, 256 heads, 16 owner pools, 256-token pages, more than 1024 units
+(rank, request) in one call, and verification rows
 whose causal limit falls before position 0 (they see nothing: lse = -inf,
 o = 0, on every rank and after the merge); a zero and a negative softmax
 scale; e4m3 with base-2 LSE.  Each compares every request's merged output
@@ -25,6 +26,14 @@ def W(**kw):
     base = dict(name="t", index=50, B=1, H=16, q_len=1, c=4, P=16, kv_dtype="bf16", lse_base="e", fixed_len=64)
     base.update(kw)
     return C.Workload(**base)
+
+
+def _ragged(n, seed, long):
+    """n short request lengths in [0, 400) (seeded) with a few long ones."""
+    lens = [int(x) for x in np.random.default_rng(seed).integers(0, 400, n)]
+    for b, L in long.items():
+        lens[b] = L
+    return lens
 
 
 CASES = [
@@ -74,6 +83,11 @@ CASES = [
     ("fp8_il64_verify", W(index=88, H=32, q_len=4, c=4, P=64, fixed_len=1500, kv_dtype="fp8", B=2,
                           interleave=64), None),
     ("fp8_il8_short", W(index=89, H=16, c=8, P=16, fixed_len=37, kv_dtype="fp8", interleave=8), None),
+    # the work plan over more than 1024 units (several 1024-unit chunks, split
+    # units in both) and at exactly 1024 ragged units (longest-first order of
+    # the single-item units)
+    ("units_over_1024", W(index=74, H=16, c=4, P=16, B=260), _ragged(260, 7, {3: 12000, 130: 8000, 259: 12000})),
+    ("units_1024_ragged", W(index=75, H=16, c=8, P=16, B=128), _ragged(128, 8, {0: 30000, 77: 9000})),
 ]
 
 
