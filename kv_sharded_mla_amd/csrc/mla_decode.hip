@@ -1092,8 +1092,14 @@ DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, in
   pl.t_max = (int32_t)std::max<int64_t>(1, (int64_t)(kMaxTab - 1) * page / kStageTok);
   pl.t_min = std::min<int32_t>(DCP_ITEM_MIN_STAGES, pl.t_max);
   pl.items_target = std::max<int32_t>(1, DCP_ITEMS_PER_CU * device_cu_count() / pl.n_row_blocks);
-  // the device plan makes at most units + max(items_target, units * ceil(stages_max / t_max)) items
-  pl.max_items = pl.units + std::max<int64_t>(pl.items_target, pl.units * ((stages_max + pl.t_max - 1) / pl.t_max));
+  // the device plan makes at most units + max(items_target, units * ceil(stages_max / t_max)) items;
+  // the item length T is at least t_min stages, so a unit of at most t_min
+  // stages is one item: with no unit longer than that the call needs no
+  // split combine
+  pl.max_items = stages_max <= pl.t_min
+                     ? pl.units
+                     : pl.units + std::max<int64_t>(pl.items_target,
+                                                    pl.units * ((stages_max + pl.t_max - 1) / pl.t_max));
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   pl.off_ws_lse = al((size_t)pl.max_items * pl.rows * kDv * sizeof(float));
   pl.off_ints = pl.off_ws_lse + al((size_t)pl.max_items * pl.rows * sizeof(float));
