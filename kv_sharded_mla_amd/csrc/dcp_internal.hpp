@@ -45,6 +45,7 @@ struct DecodePlan {
   int32_t items_target;    // work items per row block the device plan aims for
   int32_t t_min, t_max;    // item length bounds in stages
   int64_t max_items;       // bound on the items the device plan makes
+  bool direct;             // no unit longer than t_min stages: one item per unit, no plan
   size_t off_ws_lse;       // workspace: partial o, then partial lse, then the plan
   size_t off_ints;
   size_t workspace_bytes;

@@ -99,6 +99,7 @@ struct DecodeParams {
   float* lse_part;  // [units][rows]
   int32_t n_row_blocks;
   int32_t units;    // rank_count * batch
+  int32_t direct;   // every unit is one item: no work plan, item i = unit i
   // work plan (written each call by decode_plan_kernel, in the workspace)
   int32_t max_items;
   int32_t items_target;  // work items per row block the plan aims for
@@ -351,8 +352,9 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   const WgUnit wu = wg_unit(blockIdx.x, p.n_row_blocks);
   const int rb = wu.rb;
   const int64_t item = wu.unit;
-  if (item >= *p.n_items) return;
-  const int32_t unit = p.item_unit[item];
+  // without a plan (every unit is one item) item i is unit i, whole
+  if (item >= (p.direct ? (int64_t)p.units : (int64_t)*p.n_items)) return;
+  const int32_t unit = p.direct ? (int32_t)item : p.item_unit[item];
   const int b = unit % p.batch;
   const int rl = unit / p.batch;
   const int32_t ri = p.rank_begin + rl, Pi = p.page;
@@ -362,8 +364,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   // all rank-local token indices fit in int32 (seq_len is int32)
   auto visible = [&](int qi) -> int32_t { return visible_tokens(L, ri, p.c, p.interleave, p.q_len, qi, p.causal); };
   // item bounds and tile count are uniform: scalar registers
-  const int32_t j_begin = __builtin_amdgcn_readfirstlane(p.item_jb[item]);
-  const int32_t j_stop = __builtin_amdgcn_readfirstlane(p.item_je[item]);
+  const int32_t j_begin = p.direct ? 0 : __builtin_amdgcn_readfirstlane(p.item_jb[item]);
+  const int32_t j_stop = p.direct ? INT32_MAX : __builtin_amdgcn_readfirstlane(p.item_je[item]);
   const int32_t n_wg = visible((rb * MB + MB - 1) / p.heads);
   const int32_t j_end = __builtin_amdgcn_readfirstlane(min(n_wg, j_stop));
   const int32_t jlim = min(visible(row0 / p.heads), j_stop);
@@ -380,7 +382,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   // a unit with one item writes o_part / lse_part directly; the items of a
   // split unit write partials (lse in base 2) for the combine, also when this
   // row block sees none of the item's tokens (lse = -inf, o = 0)
-  const bool single = p.unit_count[unit] == 1;
+  const bool single = p.direct || p.unit_count[unit] == 1;
 
   const uint8_t* pool = p.pools + (int64_t)rl * p.pool_bytes;
   const float* spool = FP8 ? p.pool_scales + (int64_t)rl * p.cap : nullptr;
@@ -1096,7 +1098,8 @@ DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, in
   // the item length T is at least t_min stages, so a unit of at most t_min
   // stages is one item: with no unit longer than that the call needs no
   // split combine
-  pl.max_items = stages_max <= pl.t_min
+  pl.direct = stages_max <= pl.t_min;
+  pl.max_items = pl.direct
                      ? pl.units
                      : pl.units + std::max<int64_t>(pl.items_target,
                                                     pl.units * ((stages_max + pl.t_max - 1) / pl.t_max));
@@ -1153,9 +1156,15 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   prm.unit_count = prm.unit_first + pl.units;
   prm.split_units = prm.unit_count + pl.units;
   prm.dev_status = a.dev_status;
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, prm);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // a call whose units are all single items needs neither the plan nor the
+  // split combine: one kernel launch
+  prm.direct = pl.direct ? 1 : 0;
+  hipError_t e = hipSuccess;
+  if (!pl.direct) {
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, prm);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const bool aligned = a.page % kStageTok == 0;
   const int64_t grid = (pl.max_items + 7) / 8 * 8 * pl.n_row_blocks;
   const int rg = pl.row_block / 16;
@@ -1165,7 +1174,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   else
     e = rg == 4 ? launch_pc<4, false>(prm, aligned, grid, stream)
                 : (rg == 2 ? launch_pc<2, false>(prm, aligned, grid, stream) : launch_pc<1, false>(prm, aligned, grid, stream));
-  if (e != hipSuccess || pl.max_items == pl.units) return e;
+  if (e != hipSuccess || pl.direct) return e;
   // at most (max_items - units) units are split; a grid-stride loop covers them
   const int64_t pairs_max = std::min<int64_t>(pl.max_items - pl.units, pl.units) * pl.rows;
   const int64_t cgrid =
