@@ -163,7 +163,10 @@ int dcp_kv_write(const dcp_layout* layout, void* pools, float* pool_scales,
  * these sizes (0 only for invalid arguments).  max_seq_len bounds every
  * seq_len[b].  The workspace holds the call's work plan (how each (rank,
  * request) is cut into KV splits, decided on the device from seq_len) and
- * the partial outputs of requests that are split.
+ * the partial outputs of requests that are split.  When max_seq_len is short
+ * enough that no (rank, request) can be split (at most 256 tokens per rank),
+ * mla_decode_partial is one kernel launch and leaves the workspace untouched;
+ * it must still be passed.
  */
 size_t mla_decode_workspace_size(const dcp_layout* layout, int32_t rank_count, int32_t batch,
                                  int32_t q_len, int32_t heads, int64_t max_seq_len);
