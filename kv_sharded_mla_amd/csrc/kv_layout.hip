@@ -30,7 +30,7 @@ alloc_virtual_kernel(int32_t c, int32_t page, const int32_t* __restrict__ free_s
                      const int32_t* __restrict__ new_len, int32_t batch,
                      int32_t* __restrict__ block_table, int32_t bt_stride,
                      int32_t* __restrict__ dev_status) {
-  __shared__ int64_t scan[kAllocThreads];
+  __shared__ int64_t wsum[kAllocThreads / 64];
   __shared__ int flags[2];
   const int t = threadIdx.x;
   const int64_t vpage = (int64_t)page * c;
@@ -53,16 +53,24 @@ alloc_virtual_kernel(int32_t c, int32_t page, const int32_t* __restrict__ free_s
   }
   if (bad_len) atomicOr(&flags[0], 1);
   if (overflow) atomicOr(&flags[1], 1);
-  scan[t] = need;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over 1024 entries.
-  for (int off = 1; off < kAllocThreads; off <<= 1) {
-    int64_t v = (t >= off) ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += v;
-    __syncthreads();
+  // inclusive scan of the page needs: within each wave by shuffles, then
+  // over the 16 wave totals
+  const int lane = t & 63, wv = t >> 6;
+  int64_t incl = need;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
-  const int64_t total = scan[kAllocThreads - 1];
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int64_t total = 0;
+#pragma unroll
+  for (int i = 0; i < kAllocThreads / 64; ++i) {
+    const int64_t x = wsum[i];
+    if (i < wv) incl += x;
+    total += x;
+  }
   const int64_t top = *free_top;
   int code = DCP_DEV_OK;
   if (flags[0]) code = DCP_DEV_BAD_LENGTH;
@@ -72,7 +80,7 @@ alloc_virtual_kernel(int32_t c, int32_t page, const int32_t* __restrict__ free_s
     if (t == 0 && dev_status) atomicMax(dev_status, code);
     return;
   }
-  int64_t k = scan[t] - need;  // pops taken before this thread's first request
+  int64_t k = incl - need;  // pops taken before this thread's first request
   for (int b = b0; b < b1; ++b) {
     int64_t first = pages_for(old_len[b], vpage);
     int64_t nb = pages_for(new_len[b], vpage) - first;
