@@ -42,9 +42,42 @@ __device__ __forceinline__ bool merge_row4(const float* __restrict__ o, int64_t 
                                           const float* __restrict__ lse, int64_t lse_stride,
                                           int nparts, bool in_base2, int col4, f32x4& acc,
                                           float& lse_out) {
+  acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float to2 = in_base2 ? 1.0f : kLog2e;
+  if (nparts <= 8) {
+    // every partial's lse and columns are loaded at once, then the maximum
+    // is formed and the partials combined (in order r = 0, 1, ...)
+    float l[8];
+    f32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < nparts) {
+        l[k] = lse[k * lse_stride];
+        v[k] = *reinterpret_cast<const f32x4*>(o + k * o_stride + 4 * col4);
+      }
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < nparts) m = fmaxf(m, l[k]);
+    if (m == -INFINITY) {
+      lse_out = -INFINITY;
+      return false;
+    }
+    float tot = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < nparts && l[k] != -INFINITY) {
+        const float w = exp2f((l[k] - m) * to2);
+        tot += w;
+        acc += w * v[k];
+      }
+    const float inv = 1.0f / tot;
+    acc *= inv;
+    lse_out = m + (in_base2 ? log2f(tot) : logf(tot));
+    return true;
+  }
   float m = -INFINITY;
   for (int r = 0; r < nparts; ++r) m = fmaxf(m, lse[r * lse_stride]);
-  acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (m == -INFINITY) {
     lse_out = -INFINITY;
     return false;
@@ -52,7 +85,6 @@ __device__ __forceinline__ bool merge_row4(const float* __restrict__ o, int64_t 
   // work in base 2: w_r = 2^(lse2_r - m2).  The partials are loaded 8 at a
   // time before they are combined (in order r = 0, 1, ...), so the loads
   // overlap instead of each waiting for the previous one.
-  const float to2 = in_base2 ? 1.0f : kLog2e;
   float tot = 0.f;
   for (int r0 = 0; r0 < nparts; r0 += 8) {
     float l[8];
