@@ -27,8 +27,6 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]
-# optional extra compiler flags (for example -DDCP_LDS_SWIZZLE=0)
-FLAGS += os.environ.get("DCP_MLA_EXTRA_FLAGS", "").split()
 
 
 def _run(cmd):

@@ -38,47 +38,14 @@ namespace dcp {
 
 namespace {
 
-#ifndef DCP_RB_LAG
-#define DCP_RB_LAG 1
-#endif
 constexpr int kWaves = 8;     // waves per workgroup: two per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr float kTau = 8.0f;
 constexpr int kMaxTab = 512;  // page ids staged per workgroup
 constexpr int kStageTok = 32; // tokens per LDS stage
-// score fragments in token-block-major order (each accumulator then takes its
-// MFMAs back to back) or interleaved
-// split-combine workgroups per CU (a grid-stride loop covers the rest)
-#ifndef DCP_COMBINE_BLOCKS_PER_CU
-#define DCP_COMBINE_BLOCKS_PER_CU 8
-#endif
-// one work item per CU and row block instead of two when the units are about
-// equally long
-#ifndef DCP_UNIFORM_HALVES_ITEMS
-#define DCP_UNIFORM_HALVES_ITEMS 1
-#endif
-// list the single-item units of a ragged batch longest first
-#ifndef DCP_SORT_SINGLE_ITEMS
-#define DCP_SORT_SINGLE_ITEMS 1
-#endif
-// shortest work item in 32-token stages (shorter items pay their start-up
-// and partial write for little work)
-#ifndef DCP_ITEM_MIN_STAGES
-#define DCP_ITEM_MIN_STAGES 8
-#endif
-// work items the plan aims for per CU and row block
-#ifndef DCP_ITEMS_PER_CU
-#define DCP_ITEMS_PER_CU 2
-#endif
-#ifndef DCP_FP8_SCALE_PREFETCH
-#define DCP_FP8_SCALE_PREFETCH 0
-#endif
-#ifndef DCP_FP8_TBMAJOR
-#define DCP_FP8_TBMAJOR 1
-#endif
-#ifndef DCP_PC_TBMAJOR
-#define DCP_PC_TBMAJOR 1
-#endif
+constexpr int kCombineBlocksPerCu = 8;  // split-combine workgroups per CU (grid-stride beyond)
+constexpr int kItemMinStages = 8;       // shortest work item (each pays a q load and a partial write)
+constexpr int kItemsPerCu = 2;          // work items the plan aims for per CU and row block
 
 struct DecodeParams {
   const uint8_t* pools;
@@ -121,9 +88,6 @@ struct DecodeParams {
 // 72 chunks per row) or 4 (e4m3, 36 chunks) so it permutes each row.  Without
 // it the 1152- and 576-byte row strides put the 16 rows that one LDS read
 // instruction touches on the same banks.
-#ifndef DCP_LDS_SWIZZLE
-#define DCP_LDS_SWIZZLE 1
-#endif
 template <bool FP8>
 __device__ __forceinline__ int swz(int r) {
   // e4m3 rows (576 B): chunk position bit 1 from row bit 2, bit 0 from row
@@ -133,11 +97,7 @@ __device__ __forceinline__ int swz(int r) {
   // reads (rows 4G+s and 16+4G+s) conflict-free; the row bits 2 and 3^4 used
   // before cost 4 conflict cycles per K read.
   if (FP8) return ((r >> 4) & 1) | (((r >> 2) & 1) << 1);
-#if DCP_LDS_SWIZZLE == 0
-  return 2 * (((r >> 1) ^ r) & 3) + ((r >> 2) & 1);  // no conflicts with 32 banks of 4 bytes
-#else
-  return ((r >> 1) ^ r) & 7;                           // no conflicts with 64 banks of 4 bytes
-#endif
+  return ((r >> 1) ^ r) & 7;  // no conflicts with 64 banks of 4 bytes
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -373,11 +333,11 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   const int32_t jlim_s = __builtin_amdgcn_readfirstlane(jlim);
   const int n_st = j_end > j_begin ? (j_end - j_begin + STOK - 1) / STOK : 0;
   // The row blocks of one item walk its tiles from different starting points
-  // (block rb starts DCP_RB_LAG * rb tiles ahead, wrapping around): the block
+  // (block rb starts rb tiles ahead, wrapping around): the block
   // that reaches a tile first takes the miss and the others find the rows in
   // L2, instead of every block waiting on the same misses.  The order of the
   // tiles does not change the result beyond rounding.
-  const int rot = n_st > 0 ? (rb * DCP_RB_LAG) % n_st : 0;
+  const int rot = n_st > 0 ? rb % n_st : 0;
   auto tile_of = [&](int s) { const int x = s + rot; return x < n_st ? x : x - n_st; };
   // a unit with one item writes o_part / lse_part directly; the items of a
   // split unit write partials (lse in base 2) for the combine, also when this
@@ -524,7 +484,6 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
 #pragma unroll
         for (int i = 0; i < 4; ++i) tsc[4 * h + i] = v[i];
       }
-      if (DCP_FP8_SCALE_PREFETCH) __asm__ volatile("" ::: "memory");
     }
     // K fragments f = 2u + tb (k unit u, token block tb), kept PD loads ahead
     // of the MFMA that uses them; the schedule below pins that interleave.
@@ -532,9 +491,9 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
       constexpr int NF = 2 * KU, PD = 6;
       i32x4 kf[NF];
       // fragment f: k unit u of token block tb, token-block major (each
-      // accumulator's MFMAs back to back) or alternating between the blocks
-      auto ftb = [](int f) { return DCP_FP8_TBMAJOR ? f / KU : f & 1; };
-      auto fu = [](int f) { return DCP_FP8_TBMAJOR ? f % KU : f >> 1; };
+      // accumulator takes its MFMAs back to back)
+      auto ftb = [](int f) { return f / KU; };
+      auto fu = [](int f) { return f % KU; };
       auto kload = [&](int f) { return *reinterpret_cast<const i32x4*>(kv + koff[ftb(f)][0] + 64 * fu(f)); };
 #pragma unroll
       for (int f = 0; f < PD; ++f) kf[f] = kload(f);
@@ -556,8 +515,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
       // fragment f = KU*tb + u: each accumulator takes its 18 MFMAs back to back
       constexpr int NF = 2 * KU, PD = 8;
       bf16x8 kf[NF];
-      auto ftb = [](int f) { return DCP_PC_TBMAJOR ? f / KU : f & 1; };
-      auto fu = [](int f) { return DCP_PC_TBMAJOR ? f % KU : f >> 1; };
+      auto ftb = [](int f) { return f / KU; };
+      auto fu = [](int f) { return f % KU; };
       auto kload = [&](int f) {
         const int tb = ftb(f), u = fu(f);
         return *reinterpret_cast<const bf16x8*>(kv + koff[tb][u & 1] + 128 * (u >> 1));
@@ -845,7 +804,7 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   // unit is split, a partial write and its share of the combine.
   int64_t target = p.items_target;
   const bool uniform = (int64_t)st_max * p.units * 4 <= W * 5;
-  if (DCP_UNIFORM_HALVES_ITEMS && uniform) target = target > 1 ? target / 2 : 1;
+  if (uniform) target = target > 1 ? target / 2 : 1;
   int64_t T = (W + target - 1) / target;
   T = T < p.t_min ? p.t_min : (T > p.t_max ? p.t_max : T);
   auto plan_of = [&](int32_t st, int32_t& items, int32_t& len) {
@@ -877,7 +836,7 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   // short units fill the tail: a unit's rank counts the single units that
   // are longer, or as long with a lower index.
   __shared__ __attribute__((aligned(16))) int32_t s_key[1024];
-  const bool sort_singles = DCP_SORT_SINGLE_ITEMS && !uniform && p.units <= 1024;
+  const bool sort_singles = !uniform && p.units <= 1024;
   int32_t single_rank = 0;
   if (sort_singles) {
     int32_t items = 0, len = 0;
@@ -1092,8 +1051,8 @@ DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, in
   const int64_t n_r_max = (max_seq_len + cyc - 1) / cyc * interleave;
   const int64_t stages_max = (n_r_max + kStageTok - 1) / kStageTok;
   pl.t_max = (int32_t)std::max<int64_t>(1, (int64_t)(kMaxTab - 1) * page / kStageTok);
-  pl.t_min = std::min<int32_t>(DCP_ITEM_MIN_STAGES, pl.t_max);
-  pl.items_target = std::max<int32_t>(1, DCP_ITEMS_PER_CU * device_cu_count() / pl.n_row_blocks);
+  pl.t_min = std::min<int32_t>(kItemMinStages, pl.t_max);
+  pl.items_target = std::max<int32_t>(1, kItemsPerCu * device_cu_count() / pl.n_row_blocks);
   // the device plan makes at most units + max(items_target, units * ceil(stages_max / t_max)) items;
   // the item length T is at least t_min stages, so a unit of at most t_min
   // stages is one item: with no unit longer than that the call needs no
@@ -1178,7 +1137,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   // at most (max_items - units) units are split; a grid-stride loop covers them
   const int64_t pairs_max = std::min<int64_t>(pl.max_items - pl.units, pl.units) * pl.rows;
   const int64_t cgrid =
-      std::max<int64_t>(1, std::min<int64_t>(pairs_max, DCP_COMBINE_BLOCKS_PER_CU * device_cu_count()));
+      std::max<int64_t>(1, std::min<int64_t>(pairs_max, kCombineBlocksPerCu * device_cu_count()));
   hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)cgrid), dim3(256), 0, stream, prm);
   return hipGetLastError();
 }

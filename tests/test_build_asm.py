@@ -75,3 +75,14 @@ def test_non_temporal_loads_only_in_single_row_block_kernels(asm):
             assert len(nt) == len(loads), name
         else:
             assert not nt, name
+
+
+def test_no_tuning_switches_in_sources():
+    # the shipped kernels have one code path: no preprocessor switches select
+    # between tuning variants, and the build takes no extra flags from the environment
+    csrc = os.path.join(ROOT, "kv_sharded_mla_amd", "csrc")
+    for f in os.listdir(csrc):
+        text = open(os.path.join(csrc, f)).read()
+        assert not re.search(r"#\s*if(n?def)?\s+DCP_", text), f
+    build = open(os.path.join(ROOT, "kv_sharded_mla_amd", "build.py")).read()
+    assert "os.environ.get(\"DCP_" not in build
