@@ -139,15 +139,17 @@ int dcp_alloc_virtual(const dcp_layout* layout, const int32_t* free_stack, int32
  *
  * Request b appends rows cu_new[b] .. cu_new[b+1]-1 (n_b rows) at positions
  * seq_len[b]-n_b .. seq_len[b]-1 (seq_len is the length after the append).
- * Row bytes are copied unchanged (plus the e4m3 scale).  A row whose position
- * is negative (DCP_DEV_BAD_LENGTH), whose table column is >= bt_stride
+ * Row bytes are copied unchanged (plus the e4m3 scale).  A row that belongs
+ * to no request (n < cu_new[0] or n >= cu_new[batch]) or whose position is
+ * negative (DCP_DEV_BAD_LENGTH), whose table column is >= bt_stride
  * (DCP_DEV_TABLE_OVERFLOW) or whose page id is outside [0, num_pages)
  * (DCP_DEV_BAD_PAGE) is skipped and its slot_out is -1; other rows are
  * written.  Slots not addressed keep their bytes.
  *
  *   pools        c pools (see layout above), written
  *   pool_scales  float32 [c][num_pages*page] for e4m3, else NULL
- *   seq_len      int32 [batch]; cu_new int32 [batch+1] with cu_new[batch] = n_rows
+ *   seq_len      int32 [batch]; cu_new int32 [batch+1], non-decreasing, normally
+ *                with cu_new[0] = 0 and cu_new[batch] = n_rows
  *   rows         [n_rows][576] bf16 payloads, or [n_rows][576] e4m3 codes
  *   row_scales   float32 [n_rows] for e4m3, else NULL
  *   slot_out     optional int64 [n_rows]: owner * (num_pages*page) + physical slot
@@ -165,8 +167,9 @@ int dcp_kv_write(const dcp_layout* layout, void* pools, float* pool_scales,
  * request) is cut into KV splits, decided on the device from seq_len) and
  * the partial outputs of requests that are split.  When max_seq_len is short
  * enough that no (rank, request) can be split (at most 256 tokens per rank),
- * mla_decode_partial is one kernel launch and leaves the workspace untouched;
- * it must still be passed.
+ * mla_decode_partial is one kernel launch and leaves the workspace untouched:
+ * the size is then 256 bytes whatever the batch, and the buffer must still be
+ * passed.
  */
 size_t mla_decode_workspace_size(const dcp_layout* layout, int32_t rank_count, int32_t batch,
                                  int32_t q_len, int32_t heads, int64_t max_seq_len);

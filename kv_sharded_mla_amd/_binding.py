@@ -116,6 +116,43 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel=None) -> int:
     return int(t.data_ptr())
 
 
+def _bytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _need(cond: bool, msg: str):
+    """Size check before any pointer leaves Python: a short buffer would let a kernel
+    write past its end."""
+    if not cond:
+        raise ValueError(msg)
+
+
+def _row_bytes(layout: Layout) -> int:
+    return D_QK if layout.kv_dtype == KV_FP8_E4M3 else 2 * D_QK
+
+
+def _rows_of(t: torch.Tensor, layout: Layout, name: str) -> int:
+    """Number of latent rows in a [n][576] payload tensor (any element type)."""
+    if t.dim() < 1:
+        raise ValueError(f"{name} must be [n_rows][...]")
+    n = t.shape[0]
+    _need(_bytes(t) == n * _row_bytes(layout), f"{name} must hold {n} rows of {_row_bytes(layout)} bytes")
+    return n
+
+
+def _table_rows(block_table: torch.Tensor, batch: int, name: str = "block_table"):
+    _need(block_table.dim() == 2 and block_table.shape[0] >= batch, f"{name} must be [>= {batch}][stride]")
+
+
+def _pool_check(layout: Layout, pools, pool_scales, ranks: int):
+    pb = dcp_pool_bytes(layout)
+    _need(_bytes(pools) >= ranks * pb, f"pools must hold {ranks} pools of {pb} bytes")
+    if layout.kv_dtype == KV_FP8_E4M3:
+        cap = layout.num_pages * layout.page
+        _need(pool_scales is not None and pool_scales.numel() >= ranks * cap,
+              f"pool_scales must hold {ranks} x {cap} scales")
+
+
 def make_layout(c: int, page: int, num_pages: int, kv_dtype: int = KV_BF16, interleave: int = 1) -> Layout:
     return Layout(int(c), int(page), int(num_pages), int(kv_dtype), int(interleave))
 
@@ -127,6 +164,8 @@ def dcp_pool_bytes(layout: Layout) -> int:
 def dcp_alloc_virtual(layout: Layout, free_stack, free_top, old_len, new_len, block_table,
                       dev_status=None, stream=None):
     B = old_len.numel()
+    _need(new_len.numel() >= B, "new_len must hold one length per request")
+    _table_rows(block_table, B)
     lib = load_library()
     st = lib.dcp_alloc_virtual(
         ctypes.byref(layout), _ptr(free_stack, "free_stack", torch.int32), _ptr(free_top, "free_top", torch.int32, 1),
@@ -139,7 +178,11 @@ def dcp_alloc_virtual(layout: Layout, free_stack, free_top, old_len, new_len, bl
 def dcp_kv_write(layout: Layout, pools, pool_scales, block_table, seq_len, cu_new, rows, row_scales=None,
                  slot_out=None, dev_status=None, stream=None):
     B = seq_len.numel()
-    n_rows = rows.shape[0]
+    n_rows = _rows_of(rows, layout, "rows")
+    _table_rows(block_table, B)
+    _need(cu_new.numel() >= B + 1, "cu_new must hold batch + 1 offsets")
+    _need(row_scales is None or row_scales.numel() >= n_rows, "row_scales must hold one scale per row")
+    _need(slot_out is None or slot_out.numel() >= n_rows, "slot_out must hold one slot per row")
     lib = load_library()
     st = lib.dcp_kv_write(
         ctypes.byref(layout), _ptr(pools, "pools", (torch.uint8, torch.int16, torch.bfloat16)),
@@ -156,10 +199,14 @@ def dcp_kv_read(layout: Layout, pools, pool_scales, block_table, seq_len, cu_out
     """Gather positions 0 .. seq_len[b]-1 of every request into rows_out[cu_out[b] + p] (token order)."""
     B = seq_len.numel()
     payload = (torch.uint8, torch.int16, torch.bfloat16)
+    n_rows = _rows_of(rows_out, layout, "rows_out")
+    _table_rows(block_table, B)
+    _need(cu_out.numel() >= B + 1, "cu_out must hold batch + 1 offsets")
+    _need(scales_out is None or scales_out.numel() >= n_rows, "scales_out must hold one scale per row")
     st = load_library().dcp_kv_read(
         ctypes.byref(layout), _ptr(pools, "pools", payload), _ptr(pool_scales, "pool_scales", torch.float32),
         _ptr(block_table, "block_table", torch.int32), block_table.shape[-1], _ptr(seq_len, "seq_len", torch.int32),
-        _ptr(cu_out, "cu_out", torch.int32, B + 1), B, rows_out.shape[0], _ptr(rows_out, "rows_out", payload),
+        _ptr(cu_out, "cu_out", torch.int32, B + 1), B, n_rows, _ptr(rows_out, "rows_out", payload),
         _ptr(scales_out, "scales_out", torch.float32), _ptr(dev_status, "dev_status", torch.int32, 1),
         _stream(stream))
     _check("dcp_kv_read", st)
@@ -171,8 +218,14 @@ def dcp_kv_relayout(layout: Layout, src_pool, src_scales, src_block_table, seq_l
     (pages of layout.page tokens) into their owner pools (those ranks' pools, back to back)."""
     B = seq_len.numel()
     payload = (torch.uint8, torch.int16, torch.bfloat16)
-    row_bytes = D_QK if layout.kv_dtype == KV_FP8_E4M3 else 2 * D_QK
+    row_bytes = _row_bytes(layout)
     src_pages = src_pool.numel() * src_pool.element_size() // (row_bytes * layout.page)
+    _need(0 <= rank_begin and rank_count >= 1 and rank_begin + rank_count <= layout.c, "ranks outside the group")
+    _pool_check(layout, pools, pool_scales, rank_count)
+    _table_rows(block_table, B)
+    _table_rows(src_block_table, B, "src_block_table")
+    _need(src_scales is None or src_scales.numel() >= src_pages * layout.page,
+          "src_scales must hold one scale per source slot")
     st = load_library().dcp_kv_relayout(
         ctypes.byref(layout), _ptr(src_pool, "src_pool", payload), _ptr(src_scales, "src_scales", torch.float32),
         src_pages, _ptr(src_block_table, "src_block_table", torch.int32), src_block_table.shape[-1],
@@ -197,6 +250,9 @@ def mla_decode_partial(layout: Layout, pools, pool_scales, rank_begin: int, rank
         raise ValueError("q must be [batch][q_len][heads][576]")
     rows = batch * q_len * heads
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _need(0 <= rank_begin and rank_count >= 1 and rank_begin + rank_count <= layout.c, "ranks outside the group")
+    _pool_check(layout, pools, pool_scales, rank_count)
+    _table_rows(block_table, batch)
     lib = load_library()
     st = lib.mla_decode_partial(
         ctypes.byref(layout), _ptr(pools, "pools", (torch.uint8, torch.int16, torch.bfloat16)),

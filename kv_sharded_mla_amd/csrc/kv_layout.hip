@@ -120,7 +120,8 @@ kv_write_kernel(int32_t c, int32_t il, int32_t page, int32_t num_pages, uint8_t*
     const int64_t p = (int64_t)seq_len[b] - nb + (n - cu_new[b]);
     int code = DCP_DEV_OK;
     int64_t owner = 0, phys = 0;
-    if (p < 0 || nb < 0 || n >= (int64_t)cu_new[batch]) {
+    // rows outside [cu_new[0], cu_new[batch]) belong to no request
+    if (p < 0 || nb < 0 || n >= (int64_t)cu_new[batch] || n < (int64_t)cu_new[0]) {
       code = DCP_DEV_BAD_LENGTH;
     } else if (p / vpage >= bt_stride) {
       code = DCP_DEV_TABLE_OVERFLOW;

@@ -1062,6 +1062,13 @@ DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, in
                      ? pl.units
                      : pl.units + std::max<int64_t>(pl.items_target,
                                                     pl.units * ((stages_max + pl.t_max - 1) / pl.t_max));
+  if (pl.direct) {
+    // one launch that never touches the workspace: a token size that does not
+    // grow with the batch
+    pl.off_ws_lse = pl.off_ints = 0;
+    pl.workspace_bytes = 256;
+    return pl;
+  }
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   pl.off_ws_lse = al((size_t)pl.max_items * pl.rows * kDv * sizeof(float));
   pl.off_ints = pl.off_ws_lse + al((size_t)pl.max_items * pl.rows * sizeof(float));

@@ -110,19 +110,29 @@ def alloc_virtual(free_stack: np.ndarray, free_top: int, old_len: Sequence[int],
 
 
 def write_slots(block_table: np.ndarray, seq_len: Sequence[int], cu_new: Sequence[int],
-                P: int, c: int, num_pages: int, I: int = 1):
-    """Destination of every new row: (status, owner[N], phys[N]); -1 where skipped."""
+                P: int, c: int, num_pages: int, I: int = 1, n_rows: int = None):
+    """Destination of every new row: (status, owner[N], phys[N]); -1 where skipped.
+
+    Rows cu_new[b] .. cu_new[b+1]-1 belong to request b.  ``n_rows`` (default
+    cu_new[B]) is the number of rows handed over; a row that belongs to no
+    request (below cu_new[0] or at or past cu_new[B]) is skipped with
+    BAD_LENGTH.
+    """
     B = len(seq_len)
-    N = int(cu_new[B])
+    N = int(cu_new[B]) if n_rows is None else int(n_rows)
     own = np.full(N, -1, dtype=np.int64)
     phys = np.full(N, -1, dtype=np.int64)
     status = OK
+    if N > 0 and (B == 0 or int(cu_new[0]) > 0 or int(cu_new[B]) < N):
+        status = BAD_LENGTH
     stride = block_table.shape[1]
     for b in range(B):
         n_b = int(cu_new[b + 1]) - int(cu_new[b])
         first = int(seq_len[b]) - n_b
         for k in range(max(n_b, 0)):
             row = int(cu_new[b]) + k
+            if row >= N:
+                break
             p = first + k
             if first < 0:
                 status = max(status, BAD_LENGTH)
@@ -143,12 +153,13 @@ def pool_image(pools: np.ndarray, block_table: np.ndarray, seq_len, cu_new, rows
                P: int, c: int, scales: np.ndarray = None, pool_scales: np.ndarray = None, I: int = 1):
     """Expected pool bytes after scattering ``rows`` into a copy of ``pools``.
 
-    ``pools`` is [c][num_pages*P][row elements] in the stored dtype.
+    ``pools`` is [c][num_pages*P][row elements] in the stored dtype; every row
+    of ``rows`` is handed over (see :func:`write_slots`).
     """
     out = np.array(pools, copy=True)
     outs = None if pool_scales is None else np.array(pool_scales, copy=True)
     num_pages = out.shape[1] // P
-    status, own, phys = write_slots(block_table, seq_len, cu_new, P, c, num_pages, I)
+    status, own, phys = write_slots(block_table, seq_len, cu_new, P, c, num_pages, I, n_rows=len(rows))
     for n in range(len(own)):
         if own[n] >= 0:
             out[own[n], phys[n]] = rows[n]

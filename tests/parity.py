@@ -29,7 +29,7 @@ class Case:
     """One workload's inputs on host and device, and its emulated group."""
 
     def __init__(self, w: Workload, lens=None, needles=None, seed_free_stack=True, sentinel=None,
-                 num_pages=None, keep_rows=False):
+                 num_pages=None, keep_rows=False, keep_slots=False):
         from kv_sharded_mla_amd import KV_BF16, KV_FP8_E4M3
         from kv_sharded_mla_amd.group import DcpGroup
         self.w = w
@@ -50,7 +50,9 @@ class Case:
         self.rows = (data, scale) if keep_rows else None
         rows = torch.from_numpy(data.view(np.uint8).reshape(len(data), -1)).to("cuda")
         sc = torch.from_numpy(scale).to("cuda") if scale is not None else None
-        self.group.append([int(L) for L in self.lens], rows, sc)
+        # slot_out of the bulk write (owner * capacity + physical slot), kept on request
+        self.slots = torch.empty(len(data), dtype=torch.int64, device="cuda") if keep_slots else None
+        self.group.append([int(L) for L in self.lens], rows, sc, self.slots)
         del rows, sc
         torch.cuda.synchronize()
         assert self.group.status() == 0, self.group.status()

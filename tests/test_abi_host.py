@@ -91,9 +91,11 @@ def test_host_argument_errors(lib):
     assert call(base=3) == -1
     assert call(maxl=2**31) == -2
     assert call(B=0) == 0
-    # every call needs its workspace (the work plan lives there): none given
+    # every call needs its workspace (the work plan lives there, or at least a
+    # token buffer when no request can be split): none given
     assert call(maxl=1 << 20, B=1) == -4
     assert call() == -4
+    assert call(ws=256, wsb=255) == -4
     # kv write / alloc
     assert lib.dcp_kv_write(ref, 16, None, 16, 4, 16, 16, 1, 4, 8, None, None, None, None) == -3
     assert lib.dcp_kv_write(ctypes.byref(_layout(kv=1)), 16, None, 16, 4, 16, 16, 1, 4, 16, None, None, None,
@@ -104,8 +106,14 @@ def test_host_argument_errors(lib):
 
 def test_workspace_size_covers_the_work_plan(lib):
     from kv_sharded_mla_amd import mla_decode_workspace_size
-    # every call plans its work items in the workspace, so the size is never 0 for valid
-    # arguments; it holds at least one partial (512 outputs + lse, fp32) per unit and row
+    # with at most 256 tokens per rank no (rank, request) is split: one launch, no work
+    # plan, and a token size that does not grow with the batch
+    for B in (1, 64, 4096):
+        for maxl in (1, 1000, 8 * 256):
+            assert mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, B, 4, 128, maxl) == 256
+    assert mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 64, 4, 128, 8 * 256 + 1) > 256
+    # longer calls plan their work items in the workspace; it holds at least one
+    # partial (512 outputs + lse, fp32) per unit and row
     units, rows = 8 * 64, 16
     n = mla_decode_workspace_size(_layout(8, 64, 100, 0), 8, 64, 1, 16, 32768)
     assert n >= units * rows * 513 * 4
@@ -150,3 +158,56 @@ def test_layout_copy_argument_errors(lib):
     assert relayout(snp=-1) == -1 and relayout(sbts=0) == -1 and relayout(bts=0) == -1
     assert relayout(src=None) == -1 and relayout(sbt=None) == -1 and relayout(pools=None) == -1
     assert relayout(src=8) == -3 and relayout(pools=24) == -3
+
+
+def test_binding_rejects_short_buffers(lib):
+    """The Python binding checks buffer sizes before any pointer reaches a kernel: a
+    flattened payload, a short slot or scale array, or a block table with fewer rows
+    than requests is a ValueError (CPU tensors: the size check comes first)."""
+    import torch
+    import kv_sharded_mla_amd as K
+    lay = _layout(2, 16, 4, K.KV_BF16)
+    lay8 = _layout(2, 16, 4, K.KV_FP8_E4M3)
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)
+    bt, sl, cu = i32(3, 2), i32(3), i32(4)
+    rows = torch.zeros(5, 1152, dtype=torch.uint8)
+    # rows flattened to 1-D bytes: the row count would be the byte count
+    with pytest.raises(ValueError, match="rows"):
+        K.dcp_kv_write(lay, None, None, bt, sl, cu, rows.reshape(-1), None, torch.zeros(5 * 1152, dtype=torch.int64))
+    with pytest.raises(ValueError, match="rows"):
+        K.dcp_kv_write(lay8, None, None, bt, sl, cu, rows)                   # 1152-byte rows for e4m3
+    with pytest.raises(ValueError, match="slot_out"):
+        K.dcp_kv_write(lay, None, None, bt, sl, cu, rows, None, torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(ValueError, match="row_scales"):
+        K.dcp_kv_write(lay8, None, None, bt, sl, cu, torch.zeros(5, 576, dtype=torch.uint8), torch.zeros(4))
+    with pytest.raises(ValueError, match="block_table"):
+        K.dcp_kv_write(lay, None, None, i32(2, 2), sl, cu, rows)
+    with pytest.raises(ValueError, match="cu_new"):
+        K.dcp_kv_write(lay, None, None, bt, sl, i32(3), rows)
+    with pytest.raises(ValueError, match="block_table"):
+        K.dcp_alloc_virtual(lay, i32(4), i32(1), sl, sl, i32(2, 2))
+    with pytest.raises(ValueError, match="new_len"):
+        K.dcp_alloc_virtual(lay, i32(4), i32(1), sl, i32(2), bt)
+    with pytest.raises(ValueError, match="rows_out"):
+        K.dcp_kv_read(lay, None, None, bt, sl, cu, torch.zeros(7, 100, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="scales_out"):
+        K.dcp_kv_read(lay8, None, None, bt, sl, cu, torch.zeros(7, 576, dtype=torch.uint8), torch.zeros(6))
+    # decode: pools shorter than rank_count pools, missing e4m3 scales, short table
+    q = torch.zeros(3, 1, 16, 576, dtype=torch.bfloat16)
+    pb = K.dcp_pool_bytes(lay)
+    o = torch.zeros(2 * 3 * 16 * 512)
+    lse = torch.zeros(2 * 3 * 16)
+    with pytest.raises(ValueError, match="pools"):
+        K.mla_decode_partial(lay, torch.zeros(pb, dtype=torch.uint8), None, 0, 2, q, bt, sl, 64, 0.1, 0, True, o, lse)
+    with pytest.raises(ValueError, match="pool_scales"):
+        K.mla_decode_partial(lay8, torch.zeros(2 * K.dcp_pool_bytes(lay8), dtype=torch.uint8), torch.zeros(64), 0, 2,
+                             q, bt, sl, 64, 0.1, 0, True, o, lse)
+    with pytest.raises(ValueError, match="block_table"):
+        K.mla_decode_partial(lay, torch.zeros(2 * pb, dtype=torch.uint8), None, 0, 2, q, i32(2, 2), sl, 64, 0.1, 0,
+                             True, o, lse)
+    with pytest.raises(ValueError, match="ranks"):
+        K.mla_decode_partial(lay, torch.zeros(2 * pb, dtype=torch.uint8), None, 1, 2, q, bt, sl, 64, 0.1, 0, True, o,
+                             lse)
+    with pytest.raises(ValueError, match="pools"):
+        K.dcp_kv_relayout(lay, torch.zeros(16 * 1152, dtype=torch.uint8), None, i32(3, 2), sl, 0, 2,
+                          torch.zeros(pb, dtype=torch.uint8), None, bt)

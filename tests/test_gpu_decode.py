@@ -163,10 +163,13 @@ def test_query_magnitudes_far_from_one(kv, k):
 def test_query_rows_of_different_magnitudes(kv):
     # rows 2^-4 .. 2^4 apart in one 16-row block (sharp and flat softmax side
     # by side).  The score arithmetic is held to the stated lse tolerance.  A
-    # sharp row makes o close to a single V row (|o| up to ~4 here), and then
-    # the bf16 P of the PV product and the bf16 output each round by up to
-    # 2^-9 |o|, which alone can exceed the absolute 1e-2: o is held to
-    # max(stated tolerance, 2^-7 max|o|) instead.
+    # sharp row makes o close to a single V row (|o| up to ~4 here).  bf16
+    # rounding to nearest even has a relative error of at most 2^-8, and o
+    # goes through one such rounding in the fp32 partials (the bf16 P of the
+    # PV product: at most 2^-8 sum_j p_j |v_j| / l, which is |o| for a sharp
+    # row) and a second one in the merged bf16 output.  Either can exceed the
+    # absolute 1e-2, so o is held to max(stated tolerance, 2^-8 max|o|) in the
+    # partials and max(stated tolerance, 2^-7 max|o|) after the merge.
     from parity import TOL
     w = W(index=75, H=64, c=2, P=64, fixed_len=500, B=2, kv_dtype=kv)
     case = Case(w)
@@ -180,6 +183,50 @@ def test_query_rows_of_different_magnitudes(kv):
             assert np.array_equal(fin, ~np.isneginf(got_l)), name
             dl = float(np.abs(got_l[fin] - ref_l[fin]).max())
             do = float(np.abs(got_o - ref_o).max())
-            bound = max(to, 2.0 ** -7 * float(np.abs(ref_o).max()))
+            bound = max(to, 2.0 ** (-7 if name == "merged" else -8) * float(np.abs(ref_o).max()))
             log(f"{kv} b={b} {name}: max|do|={do:.3e} (bound {bound:.3e}) max|dlse|={dl:.3e} (tol {tl})")
             assert dl <= tl and do <= bound, (name, do, bound, dl)
+
+
+# One real rank's call: rank_begin = r, rank_count = 1 on that rank's own pool (and
+# sub-ranges of the emulated group).  The kernel judges visibility with the global
+# rank r but reads pool, scales and outputs at the local index; every rank's
+# partial must still be the oracle's striped partial of rank r (SGLang page,
+# "MLA decode dataflow": each rank returns its own o_r, lse_r).
+RANK_CASES = [
+    # name, workload, lengths, short (single launch, no work plan)
+    ("bf16_direct", W(index=100, H=64, c=4, P=64, fixed_len=900, B=3), None, True),
+    ("bf16_split", W(index=101, H=64, c=8, P=64, fixed_len=30000, B=2), None, False),
+    ("fp8_direct", W(index=102, H=64, c=8, P=64, fixed_len=1500, kv_dtype="fp8", B=2), None, True),
+    ("fp8_split", W(index=103, H=64, c=4, P=64, fixed_len=40000, kv_dtype="fp8"), None, False),
+    ("il16_verify_q4", W(index=104, H=16, q_len=4, c=8, P=64, fixed_len=1777, B=2, interleave=16), None, True),
+    ("il16_verify_q4_split", W(index=105, H=16, q_len=4, c=8, P=64, fixed_len=25000, interleave=16), None, False),
+    ("h128_verify_ragged", W(index=106, H=128, q_len=4, c=6, P=32, B=3), [700, 9000, 5], False),
+]
+
+
+@pytest.mark.parametrize("name,w,lens,short", RANK_CASES, ids=[c[0] for c in RANK_CASES])
+def test_rank_subset_calls(name, w, lens, short):
+    from kv_sharded_mla_amd import LSE_BASE_2, LSE_BASE_E
+    from parity import compare
+    case = Case(w, lens=lens)
+    o_full, l_full, _, _ = case.run()
+    base = LSE_BASE_2 if w.lse_base == "2" else LSE_BASE_E
+    ranges = [(1, 1), (w.c - 1, 1), (0, 1)] + ([(2, 3)] if w.c >= 5 else [])
+    refs = [case.oracle(b) for b in range(w.B)]
+    for rb, rc in ranges:
+        o_p, l_p = case.group.decode(case.q, w.sm_scale, base, w.causal, rank_begin=rb, rank_count=rc)
+        import torch
+        torch.cuda.synchronize()
+        assert case.group.status() == 0
+        o_p, l_p = o_p.cpu().numpy(), l_p.cpu().numpy()
+        assert o_p.shape[0] == rc
+        for b in range(w.B):
+            _, _, rop, rlp = refs[b]
+            compare(f"{name} ranks [{rb}, {rb + rc}) b={b}", o_p[:, b], l_p[:, b], rop[rb:rb + rc], rlp[rb:rb + rc],
+                    w.kv_dtype, partial=True)
+        if short:
+            # without a work plan every (rank, request) is one workgroup doing the same
+            # arithmetic in either call: bit for bit
+            assert np.array_equal(o_p.view(np.uint32), o_full[rb:rb + rc].view(np.uint32))
+            assert np.array_equal(l_p.view(np.uint32), l_full[rb:rb + rc].view(np.uint32))

@@ -23,13 +23,16 @@ def _t(a, dtype=torch.int32):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype)
 
 
-@pytest.mark.parametrize("seed", range(6))
-def test_alloc_matches_oracle_over_growth(seed):
+@pytest.mark.parametrize("seed,B", [(s, None) for s in range(6)] + [(6, 65), (7, 1000), (8, 1025), (9, 4097)])
+def test_alloc_matches_oracle_over_growth(seed, B):
+    """Block table and free-stack top bit-exact over four growth steps.  Batches of
+    65 and 1000 requests span several waves of the allocator's scan (the carry over
+    the wave totals); 1025 and 4097 give every thread several requests."""
     K = _lib()
     rng = np.random.default_rng(seed)
     c = int(rng.integers(1, 9))
     P = int(rng.choice([1, 2, 16, 64]))
-    B = int(rng.integers(1, 40))
+    B = int(rng.integers(1, 40)) if B is None else B
     final = rng.integers(0, 5000, size=B)
     vp = P * c
     num_pages = int(sum((L + vp - 1) // vp for L in final)) + 3
@@ -70,6 +73,64 @@ def test_alloc_errors_leave_state(old, new, top, stride, code):
     assert int(status.item()) == code
     assert int(d_top.item()) == top
     assert (d_bt.cpu().numpy() == -7).all()
+
+
+@pytest.mark.parametrize("B,needy", [(1025, 1020), (4097, 3000), (200, 130)])
+def test_alloc_out_of_pages_in_a_later_wave(B, needy):
+    # only one request, owned by a thread beyond the first wave, needs pages, and
+    # one more than the stack holds: all or nothing, nothing changes
+    K = _lib()
+    c, P = 2, 4
+    old = np.full(B, 8, np.int64)
+    new = old.copy()
+    new[needy] = 8 + 5 * P * c          # five more virtual pages
+    top = 4
+    layout = K.make_layout(c, P, 10, K.KV_BF16)
+    d_top = _t([top])
+    d_bt = _t(np.full((B, 8), -7, np.int32))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.dcp_alloc_virtual(layout, _t(np.arange(10, dtype=np.int32)), d_top, _t(old), _t(new), d_bt, status)
+    st, h_top, h_bt = OL.alloc_virtual(np.arange(10, dtype=np.int32), top, old, new, np.full((B, 8), -7, np.int32),
+                                       P, c)
+    assert st == OL.OUT_OF_PAGES and int(status.item()) == OL.OUT_OF_PAGES
+    assert int(d_top.item()) == h_top == top
+    assert np.array_equal(d_bt.cpu().numpy(), h_bt) and (h_bt == -7).all()
+    # with one more page on the stack the same call succeeds and takes exactly those five
+    d_top = _t([5])
+    status.zero_()
+    K.dcp_alloc_virtual(layout, _t(np.arange(10, dtype=np.int32)), d_top, _t(old), _t(new), d_bt, status)
+    st, h_top, h_bt = OL.alloc_virtual(np.arange(10, dtype=np.int32), 5, old, new, np.full((B, 8), -7, np.int32),
+                                       P, c)
+    assert st == OL.OK and int(status.item()) == 0 and int(d_top.item()) == h_top == 0
+    assert np.array_equal(d_bt.cpu().numpy(), h_bt)
+
+
+def test_kv_write_rows_below_the_first_offset_belong_to_no_request():
+    # cu_new[0] > 0: rows 0 .. cu_new[0]-1 belong to no request; they are skipped
+    # with BAD_LENGTH and slot -1 (never written over a cached token of request 0)
+    K = _lib()
+    c, P = 2, 4
+    lens = np.array([12, 7])
+    vp = P * c
+    bt = np.array([[2, 0], [1, -1]], np.int32)
+    cu = np.array([3, 6, 8])            # request 0 appends rows 3..5, request 1 rows 6..7
+    N = 8
+    rng = np.random.default_rng(9)
+    rows = rng.integers(0, 65536, size=(N, 576)).astype(np.uint16)
+    pools = np.full((c, 3 * P, 576), 0x5A5A, np.uint16)
+    est, own, phys, want, _ = OL.pool_image(pools, bt, lens, cu, rows, P, c)
+    assert est == OL.BAD_LENGTH and (own[:3] == -1).all() and (own[3:] >= 0).all()
+    layout = K.make_layout(c, P, 3, K.KV_BF16)
+    d_pools = torch.from_numpy(pools.view(np.uint8).reshape(-1).copy()).to("cuda")
+    slot = torch.full((N,), -99, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.dcp_kv_write(layout, d_pools, None, _t(bt), _t(lens), _t(cu),
+                   torch.from_numpy(rows.view(np.uint8).copy()).to("cuda"), None, slot, status)
+    assert int(status.item()) == OL.BAD_LENGTH
+    assert np.array_equal(d_pools.cpu().numpy().view(np.uint16).reshape(c, -1, 576), want)
+    s = slot.cpu().numpy()
+    cap = 3 * P
+    assert (s[:3] == -1).all() and np.array_equal(s[3:], own[3:] * cap + phys[3:])
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])

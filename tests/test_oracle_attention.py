@@ -141,12 +141,53 @@ def test_brute_force_fsum(seed, q_len, L, causal):
                 assert abs(o[i, h, d] - ref) < 1e-12
 
 
+@pytest.mark.parametrize("L,q_len,c", [(1, 8, 1), (2, 8, 3), (5, 8, 4), (3, 4, 2), (6, 8, 8)])
+def test_rows_that_see_no_position_brute_force(L, q_len, c):
+    # causal verification with fewer tokens than query rows: row i sits at
+    # position L - q_len + i and sees p <= L - q_len + i, so rows with i <
+    # q_len - L see nothing.  Brute force over the visible set (math.fsum), for
+    # the full context and for every rank's striped share p mod c = r: an empty
+    # set gives lse = -inf and o = 0, the others the plain softmax.
+    rng = np.random.default_rng(400 + 10 * L + q_len + c)
+    H = 2
+    q, kv = _case(rng, q_len, H, L)
+    qf = bf16_to_f64(q)
+    K = bf16_to_f64(kv[0])
+    o_full, lse_full = A.decode_attention(q, kv, L, SCALE, causal=True)
+    o_p, lse_p = A.rank_partials(q, kv, L, SCALE, c, causal=True)
+
+    def brute(i, h, positions):
+        if not positions:
+            return None, -math.inf
+        s = [SCALE * math.fsum(float(qf[i, h, d]) * float(K[p, d]) for d in range(576)) for p in positions]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        z = math.fsum(w)
+        o = [math.fsum(w[k] * float(K[p, d]) for k, p in enumerate(positions)) / z for d in range(512)]
+        return np.array(o), m + math.log(z)
+
+    n_empty = 0
+    for i in range(q_len):
+        last = L - q_len + i
+        for h in range(H):
+            for r in [None] + list(range(c)):
+                pos = [p for p in range(L) if p <= last and (r is None or p % c == r)]
+                o_ref, l_ref = brute(i, h, pos)
+                o_got, l_got = (o_full[i, h], lse_full[i, h]) if r is None else (o_p[r, i, h], lse_p[r, i, h])
+                if o_ref is None:
+                    n_empty += r is None
+                    assert l_got == -math.inf and not o_got.any(), (i, h, r)
+                else:
+                    assert abs(l_got - l_ref) < 1e-12 and np.abs(o_got - o_ref).max() < 1e-12, (i, h, r)
+    assert n_empty == H * (q_len - L)
+
+
 @pytest.mark.parametrize("c", range(1, 9))
 @pytest.mark.parametrize("L", [1, 3, 7, 64, 130])
 @pytest.mark.parametrize("q_len,base", [(1, "e"), (4, "2")])
 def test_striped_merge_equals_full(c, L, q_len, base):
-    if q_len > L:
-        pytest.skip("more query rows than tokens")
+    # with q_len > L the first verification rows see no position at all: their
+    # full attention and every partial are (o = 0, lse = -inf), and so is the merge
     rng = np.random.default_rng(c * 1000 + L + q_len)
     q, kv = _case(rng, q_len, 3, L)
     o_full, lse_full = A.decode_attention(q, kv, L, SCALE, causal=True, base=base)
@@ -155,8 +196,12 @@ def test_striped_merge_equals_full(c, L, q_len, base):
         if r >= L:
             assert np.all(np.isneginf(lse_p[r])) and not o_p[r].any()
     o, lse = A.merge(o_p, lse_p, base)
+    empty = np.isneginf(lse_full)
+    assert np.array_equal(np.isneginf(lse), empty)
+    assert empty.sum() == 3 * max(0, q_len - L)
+    assert not o[empty].any() and not o_full[empty].any()
     assert np.abs(o - o_full).max() < 1e-12
-    assert np.abs(lse - lse_full).max() < 1e-12
+    assert np.abs(lse[~empty] - lse_full[~empty]).max(initial=0.0) < 1e-12
     if c == 1:
         assert np.array_equal(o_p[0], o_full) and np.array_equal(lse_p[0], lse_full)
 

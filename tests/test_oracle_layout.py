@@ -413,3 +413,65 @@ def test_read_rows_span_outside_the_output_is_skipped():
     assert st == layout.BAD_LENGTH and (out == 0xEEEE).all()
     st, out, _ = layout.read_rows(pools, bt, [3], [1, 4], P, c, out=sentinel)
     assert st == layout.OK and (out[0] == 0xEEEE).all() and not (out[1:] == 0xEEEE).any()
+
+
+# ---- planted mistakes in the gather and the relayout -------------------------
+# A copy of read_rows or relayout_dense with one plausible bug (made by editing
+# its source text) replaces the oracle function while the pins above run: at
+# least one pin must fail for every mutant.
+
+_READ_PINS = [
+    lambda: [test_read_rows_restores_token_order(*a) for a in [
+        (4, 2, 1, [22, 0, 9]), (2, 4, 2, [17, 8]), (3, 6, 3, [40, 1, 18]), (8, 16, 4, [300]), (1, 4, 1, [13, 4]),
+        (4, 8, 8, [70, 33])]],
+    lambda: [test_read_rows_inverts_the_scatter(s) for s in range(6)],
+    lambda: test_read_rows_errors_skip_and_keep(),
+    lambda: test_read_rows_span_outside_the_output_is_skipped(),
+]
+_RELAYOUT_PINS = [
+    lambda: [test_relayout_places_exactly_the_owned_rows(*a) for a in [
+        (4, 2, 1, [22, 0, 9]), (2, 4, 2, [17, 8]), (3, 6, 3, [40, 1, 18]), (8, 16, 16, [300, 5]),
+        (1, 4, 1, [13, 4])]],
+    lambda: test_relayout_rank_ranges_compose(),
+    lambda: test_relayout_to_one_rank_is_the_page_copy(),
+    lambda: test_relayout_errors(),
+]
+
+_MUTANTS = {
+    # the interleave size ignored when locating a position
+    "read_interleave_ignored": ("read_rows", "r, s = slot_of(block_table[b], p, P, c, I)",
+                                "r, s = slot_of(block_table[b], p, P, c, 1)"),
+    # the output span no longer checked against the output rows
+    "read_span_check_dropped": ("read_rows",
+                                "if L < 0 or int(cu_out[b]) < 0 or int(cu_out[b + 1]) > n_out or int(cu_out[b + 1]) - int(cu_out[b]) != L:",
+                                "if L < 0 or int(cu_out[b + 1]) - int(cu_out[b]) != L:"),
+    # the source slot one position off inside its page
+    "relayout_shifted_source_slot": ("relayout_dense", "out[r, s] = src_pool[sp * P + p % P]",
+                                     "out[r, s] = src_pool[sp * P + (p + 1) % P]"),
+    # the rank filter of a partial call taken with interleave 1
+    "relayout_rank_filter_token_cycle": ("relayout_dense",
+                                         "if not rank_begin <= owner(p, c, I) < rank_begin + rank_count:",
+                                         "if not rank_begin <= owner(p, c, 1) < rank_begin + rank_count:"),
+    # one row past the exact token count (a stale row of a partial last page)
+    "relayout_one_extra_row": ("relayout_dense", "        for p in range(L):\n            # the owner",
+                               "        for p in range(L + 1):\n            # the owner"),
+}
+
+
+@pytest.mark.parametrize("kind", sorted(_MUTANTS))
+def test_planted_gather_and_relayout_mistakes_fail_a_pin(kind, monkeypatch):
+    import inspect
+    import textwrap
+    fn, old, new = _MUTANTS[kind]
+    src = textwrap.dedent(inspect.getsource(getattr(layout, fn)))
+    assert src.count(old) == 1, (kind, "mutation does not apply")
+    ns = dict(vars(layout))
+    exec(compile(src.replace(old, new), f"<mutant {kind}>", "exec"), ns)
+    monkeypatch.setattr(layout, fn, ns[fn])
+    failed = 0
+    for pin in (_READ_PINS if fn == "read_rows" else _RELAYOUT_PINS):
+        try:
+            pin()
+        except Exception:      # an assertion, or an index past the output the real code never writes
+            failed += 1
+    assert failed >= 1, kind
