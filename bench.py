@@ -10,7 +10,12 @@ in alternation so consecutive steps never find the previous step's KV in the
 
 Prints one JSON line (rank 0).  Progress goes to stderr.
 
-    python bench.py [--config tplocal] [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--config replq] [--extras tiny,tplocal,verify,long] [--steps K] [--warmup W] [--gpus 1]
+
+The headline line is the replicated-q workload (128 heads, 32 ragged requests
+up to 256K tokens, the largest of the five that one GPU holds); the same run
+times the other workloads and reports each under "workloads": decode time,
+roofline fractions and the one-rank share.
 
 With --op read or --op relayout it times instead the extend gather
 (dcp_kv_read: all cached rows of the workload back to token order) or the
@@ -125,47 +130,31 @@ def cpu_baseline(w, lens, budget_s: float):
             "seconds": round(t_total, 2), "cpu_model": host_info()[0], "blas": host_info()[1]}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="tplocal")
-    ap.add_argument("--copies", type=int, default=2, help="pool copies used in rotation")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--interleave", type=int, default=None,
-                    help="KV interleave size I (a divisor of the page size; the workload's own by default)")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="after timing, copy a buffer of this many MiB once (HBM counter calibration)")
-    ap.add_argument("--no-share", action="store_true",
-                    help="skip timing one rank's share (profiling runs that should hold only group launches)")
-    ap.add_argument("--op", choices=("step", "read", "relayout"), default="step",
-                    help="what to time: the decode layer-step (default) or one of the layout copies")
-    ap.add_argument("--decode-only", type=int, default=0,
-                    help="after the timed steps, launch the decode entry point this many more times (profiling)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; the c-rank DCP group is emulated on that GPU "
-              "(--gpus 1).", file=sys.stderr)
-        sys.exit(2)
+HEADLINE = "replq"        # the largest single-GPU workload: 128 heads, ragged contexts up to 256K
+EXTRAS = ("tiny", "tplocal", "verify", "long")
 
+
+def roofline_of(w, flops, nbytes, t_ms):
+    """Fractions of the MI355X peaks for one launch of t_ms: HBM GB/s and bf16 MFMA TFLOP/s;
+    the 128-head workloads are judged on MFMA, the others on HBM."""
+    gbps = nbytes / (t_ms * 1e-3) / 1e9
+    tflops = flops / (t_ms * 1e-3) / 1e12
+    mfma_bound = w.H * w.q_len >= 128
+    return dict(bound="mfma" if mfma_bound else "hbm", gbps=gbps, tflops=tflops,
+                hbm_frac=gbps / HBM_PEAK_GBPS, mfma_frac=tflops / MFMA_BF16_PEAK_TFLOPS,
+                frac=(tflops / MFMA_BF16_PEAK_TFLOPS) if mfma_bound else (gbps / HBM_PEAK_GBPS))
+
+
+def time_workload(w, steps, warmup, copies=2, share=True, decode_only=0, calib_copy_mib=0):
+    """Time `steps` layer-steps of workload w on resident pools; returns the measurements."""
     import numpy as np
     import torch
 
     import kv_sharded_mla_amd as K
     from kv_sharded_mla_amd.group import DcpGroup
-    from workloads import accounting, configs, gen
+    from workloads import accounting, gen
 
-    w = configs.BY_NAME[args.config]
-    if args.interleave is not None:
-        w = configs.scaled(w, interleave=args.interleave, name=w.name)
-    if args.op != "step":
-        return bench_copy(args, w)
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    K.load_library()
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     lens = gen.lengths(w)
     ctx = np.maximum(lens - w.q_len, 0)           # resident context before the step's new tokens
     num_pages = gen.pool_pages(w, lens)
@@ -190,7 +179,7 @@ def main():
     ctx_rows = torch.from_numpy(row_u8[ctx_idx]).to(dev)
     ctx_sc = torch.from_numpy(scale[ctx_idx]).to(dev) if scale is not None else None
     del data, scale, row_u8
-    for k in range(args.copies):
+    for k in range(copies):
         g = DcpGroup(w.c, w.P, num_pages, kv_kind, w.B, stride, free_stack=stack, device="cuda:0",
                      interleave=w.interleave)
         g.append([int(x) for x in ctx], ctx_rows, ctx_sc)
@@ -198,7 +187,7 @@ def main():
     del ctx_rows, ctx_sc
     torch.cuda.synchronize()
     assert all(g.status() == 0 for g in groups)
-    log(f"{args.copies} resident pool copies written ({groups[0].pools.numel() * args.copies / 2**30:.2f} GiB)")
+    log(f"{copies} resident pool copies written ({groups[0].pools.numel() * copies / 2**30:.2f} GiB)")
 
     q = torch.from_numpy(gen.q_bits(w).view(np.int16)).to(dev)
     old_len = torch.from_numpy(ctx.astype(np.int32)).to(dev)
@@ -208,7 +197,7 @@ def main():
     for g in groups:
         g.max_seq_len = max_len
     ws_bytes = K.mla_decode_workspace_size(groups[0].layout, w.c, w.B, w.q_len, w.H, max_len)
-    ws = torch.empty(max(ws_bytes // 4, 4), dtype=torch.float32, device=dev) if ws_bytes else None
+    ws = torch.empty(max(ws_bytes // 4, 4), dtype=torch.float32, device=dev)
     o_part = torch.empty((w.c, w.B, w.q_len, w.H, K.D_V), dtype=torch.float32, device=dev)
     lse_part = torch.empty((w.c, w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
     o = torch.empty((w.B, w.q_len, w.H, K.D_V), dtype=torch.bfloat16, device=dev)
@@ -219,11 +208,12 @@ def main():
     need_pages = int(sum((int(L) + vp - 1) // vp - (int(x) + vp - 1) // vp for L, x in zip(lens, ctx)))
     saved_top = [g.free_top.clone() for g in groups]
 
-    def step(g, ev=None):
+    def step(gi, ev=None):
+        g = groups[gi]
         if ev is not None:
             ev[0].record(stream)
         if need_pages:
-            g.free_top.copy_(saved_top[groups.index(g)])
+            g.free_top.copy_(saved_top[gi])
         K.dcp_alloc_virtual(g.layout, g.free_stack, g.free_top, old_len, new_len, g.block_table, g.dev_status)
         K.dcp_kv_write(g.layout, g.pools, g.pool_scales, g.block_table, new_len, cu_new, new_rows, new_sc, None,
                        g.dev_status)
@@ -237,81 +227,150 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    for i in range(args.warmup):
-        step(groups[i % len(groups)])
+    for i in range(warmup):
+        step(i % len(groups))
     torch.cuda.synchronize()
     assert all(g.status() == 0 for g in groups), [g.status() for g in groups]
     for g in groups:
         g.seq_len = new_len.clone()
-    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+    log(f"warmup {warmup} steps done; timing {steps} steps")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(groups[i % len(groups)], evs[i])
+    for i in range(steps):
+        step(i % len(groups), evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     assert all(g.status() == 0 for g in groups), [g.status() for g in groups]
-    t_write = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    t_dec = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    t_merge = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-    t_step = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
-    log(f"per step: wall {ms_per_step * 1e3:.1f} us; events: write {t_write * 1e3:.1f} us, decode "
-        f"{t_dec * 1e3:.1f} us, merge {t_merge * 1e3:.1f} us, step {t_step * 1e3:.1f} us")
+    r = dict(lens=lens, max_len=max_len, wall_ms=wall * 1e3 / steps)
+    r["t_write"] = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    r["t_dec"] = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    r["t_merge"] = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    r["t_step"] = evs[0][0].elapsed_time(evs[-1][3]) / steps
     dec_each = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    dec_med = dec_each[len(dec_each) // 2]
-    dec_p90 = dec_each[min(len(dec_each) - 1, (9 * len(dec_each)) // 10)]
+    r["dec_med"] = dec_each[len(dec_each) // 2]
+    r["dec_p90"] = dec_each[min(len(dec_each) - 1, (9 * len(dec_each)) // 10)]
+    log(f"per step: wall {r['wall_ms'] * 1e3:.1f} us; events: write {r['t_write'] * 1e3:.1f} us, decode "
+        f"{r['t_dec'] * 1e3:.1f} us, merge {r['t_merge'] * 1e3:.1f} us, step {r['t_step'] * 1e3:.1f} us")
     # one real rank's share: rank 0's pool alone (rank_begin 0, rank_count 1), as one GPU
-    # of a c-GPU group would run it
-    g = groups[0]
-    share = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-    n_share = 0 if args.no_share else len(share)
-    for k in range(-2 if n_share else 0, n_share):
-        if k >= 0:
-            share[k][0].record(stream)
-        K.mla_decode_partial(g.layout, g.pools, g.pool_scales, 0, 1, q, g.block_table, new_len, max_len,
-                             w.sm_scale, base, w.causal, o_part[:1], lse_part[:1], ws, g.dev_status)
-        if k >= 0:
-            share[k][1].record(stream)
-    torch.cuda.synchronize()
-    assert g.status() == 0, g.status()
-    t_share = None if args.no_share else sorted(a.elapsed_time(b) for a, b in share)[len(share) // 2]
-    log(f"decode median {dec_med * 1e3:.1f} us, p90 {dec_p90 * 1e3:.1f} us"
-        + ("" if t_share is None else f"; one rank's share {t_share * 1e3:.1f} us"))
-    for i in range(args.decode_only):
+    # of a c-GPU group would run it (its own, smaller work plan)
+    r["t_share"] = None
+    if share:
+        g = groups[0]
+        ws1 = torch.empty(max(K.mla_decode_workspace_size(g.layout, 1, w.B, w.q_len, w.H, max_len) // 4, 4),
+                          dtype=torch.float32, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for k in range(-2, len(ev)):
+            if k >= 0:
+                ev[k][0].record(stream)
+            K.mla_decode_partial(g.layout, g.pools, g.pool_scales, 0, 1, q, g.block_table, new_len, max_len,
+                                 w.sm_scale, base, w.causal, o_part[:1], lse_part[:1], ws1, g.dev_status)
+            if k >= 0:
+                ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        assert g.status() == 0, g.status()
+        r["t_share"] = sorted(a.elapsed_time(b) for a, b in ev)[len(ev) // 2]
+    log(f"decode median {r['dec_med'] * 1e3:.1f} us, p90 {r['dec_p90'] * 1e3:.1f} us"
+        + ("" if r["t_share"] is None else f"; one rank's share {r['t_share'] * 1e3:.1f} us"))
+    for i in range(decode_only):
         g = groups[i % len(groups)]
         K.mla_decode_partial(g.layout, g.pools, g.pool_scales, 0, w.c, q, g.block_table, new_len, max_len,
                              w.sm_scale, base, w.causal, o_part, lse_part, ws, g.dev_status)
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib << 20
+    if calib_copy_mib:
+        n = calib_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty(n, dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
         dst.copy_(src)
         del src, dst
     torch.cuda.synchronize()
+    del groups, o_part, lse_part, o, lse, ws, q
+    torch.cuda.empty_cache()
+    r["acct"] = accounting.layer_step(w, lens)
+    r["share_acct"] = accounting.rank_share(w, lens, 0)
+    return r
 
-    acct = accounting.layer_step(w, lens)
+
+def summary_of(w, r):
+    """Per-workload figures of the JSON line (decode us, roofline fractions, one rank's share)."""
+    acct, sh = r["acct"], r["share_acct"]
+    roof = roofline_of(w, acct["flops"], acct["decode_bytes"], r["t_dec"])
+    out = {"workload": w.name, "decode_us": round(r["t_dec"] * 1e3, 2),
+           "decode_median_us": round(r["dec_med"] * 1e3, 2), "decode_p90_us": round(r["dec_p90"] * 1e3, 2),
+           "us_per_layer_step": round(r["wall_ms"] * 1e3, 2), "bound": roof["bound"], "frac": round(roof["frac"], 4),
+           "hbm_frac": round(roof["hbm_frac"], 4), "mfma_frac": round(roof["mfma_frac"], 4),
+           "decode_gbps": round(roof["gbps"], 1), "decode_tflops": round(roof["tflops"], 2)}
+    if r["t_share"] is not None:
+        sr = roofline_of(w, sh["flops"], sh["decode_bytes"], r["t_share"])
+        out.update({"one_rank_share_us": round(r["t_share"] * 1e3, 2), "one_rank_share_frac": round(sr["frac"], 4),
+                    "one_rank_share_hbm_frac": round(sr["hbm_frac"], 4)})
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=HEADLINE, help="workload of the headline line")
+    ap.add_argument("--extras", default=",".join(EXTRAS),
+                    help="other workloads timed in the same run and reported under 'workloads' ('' for none)")
+    ap.add_argument("--extra-steps", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=2, help="pool copies used in rotation")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--interleave", type=int, default=None,
+                    help="KV interleave size I (a divisor of the page size; the workload's own by default)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB once (HBM counter calibration)")
+    ap.add_argument("--no-share", action="store_true",
+                    help="skip timing one rank's share (profiling runs that should hold only group launches)")
+    ap.add_argument("--op", choices=("step", "read", "relayout"), default="step",
+                    help="what to time: the decode layer-step (default) or one of the layout copies")
+    ap.add_argument("--decode-only", type=int, default=0,
+                    help="after the timed steps, launch the decode entry point this many more times (profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; the c-rank DCP group is emulated on that GPU "
+              "(--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kv_sharded_mla_amd as K
+    from workloads import configs
+
+    w = configs.BY_NAME[args.config]
+    if args.interleave is not None:
+        w = configs.scaled(w, interleave=args.interleave, name=w.name)
+    if args.op != "step":
+        return bench_copy(args, w)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K.load_library()
+    torch.cuda.set_device(0)
+
+    r = time_workload(w, args.steps, args.warmup, args.copies, not args.no_share, args.decode_only,
+                      args.calib_copy_mib)
+    acct = r["acct"]
+    lens, max_len = r["lens"], r["max_len"]
+    ms_per_step = r["wall_ms"]
     kv_gbps = acct["kv_bytes"] / (ms_per_step * 1e-3) / 1e9
     tflops = acct["flops"] / (ms_per_step * 1e-3) / 1e12
-    dec_gbps = acct["decode_bytes"] / (t_dec * 1e-3) / 1e9
-    dec_tflops = acct["flops"] / (t_dec * 1e-3) / 1e12
-    mfma_bound = w.H * w.q_len >= 128
-    if mfma_bound:
-        roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dec_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    rf = roofline_of(w, acct["flops"], acct["decode_bytes"], r["t_dec"])
+    if rf["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": round(rf["tflops"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(rf["frac"], 4)}
     else:
-        roof = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4)}
+        roof = {"bound": "hbm", "achieved": round(rf["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(rf["frac"], 4)}
     roof["traffic"] = load_traffic(w.name)
-    roof["kernel"] = "mla_decode_partial (mla_decode_kernel + split combine when splits > 1)"
+    roof["kernel"] = "mla_decode_partial (decode kernel + work plan and split combine when units split)"
     roof["algorithmic_bytes_per_launch"] = acct["decode_bytes"]
     roof["flops_per_launch"] = acct["flops"]
-    roof["hbm_frac"] = round(dec_gbps / HBM_PEAK_GBPS, 4)
-    roof["mfma_frac"] = round(dec_tflops / MFMA_BF16_PEAK_TFLOPS, 4)
-    roof["launch_us"] = round(t_dec * 1e3, 2)
+    roof["hbm_frac"] = round(rf["hbm_frac"], 4)
+    roof["mfma_frac"] = round(rf["mfma_frac"], 4)
+    roof["launch_us"] = round(r["t_dec"] * 1e3, 2)
 
     out = {
         "metric": "DCP MLA decode: achieved KV GB/s & % roofline; TFLOP/s; us per layer-step",
@@ -332,13 +391,22 @@ def main():
                    "lse_base": w.lse_base, "emulated_ranks_on_one_gpu": w.c},
         "us_per_layer_step": round(ms_per_step * 1e3, 2),
         "tflops": round(tflops, 2),
-        "kernel_us": {"alloc+kv_write": round(t_write * 1e3, 2), "mla_decode_partial": round(t_dec * 1e3, 2),
-                      "dcp_lse_merge": round(t_merge * 1e3, 2),
-                      "mla_decode_partial_median": round(dec_med * 1e3, 2),
-                      "mla_decode_partial_p90": round(dec_p90 * 1e3, 2),
-                      "one_rank_share_decode": None if t_share is None else round(t_share * 1e3, 2)},
+        "kernel_us": {"alloc+kv_write": round(r["t_write"] * 1e3, 2), "mla_decode_partial": round(r["t_dec"] * 1e3, 2),
+                      "dcp_lse_merge": round(r["t_merge"] * 1e3, 2),
+                      "mla_decode_partial_median": round(r["dec_med"] * 1e3, 2),
+                      "mla_decode_partial_p90": round(r["dec_p90"] * 1e3, 2),
+                      "one_rank_share_decode": None if r["t_share"] is None else round(r["t_share"] * 1e3, 2)},
         "roofline": roof,
     }
+    if r["t_share"] is not None:
+        out["one_rank_share"] = {k: v for k, v in summary_of(w, r).items() if k.startswith("one_rank")}
+    extras = [x for x in args.extras.split(",") if x and x != w.name]
+    if extras:
+        out["workloads"] = {}
+        for name in extras:
+            we = configs.BY_NAME[name]
+            re_ = time_workload(we, args.extra_steps, min(args.warmup, 5), args.copies, not args.no_share)
+            out["workloads"][name] = summary_of(we, re_)
     if not args.no_cpu_baseline:
         log(f"timing the oracle on the host for about {args.cpu_budget:.0f} s")
         out["cpu_baseline"] = cpu_baseline(w, lens, args.cpu_budget)

@@ -60,3 +60,17 @@ def test_workload_intensities():
     # q_len 4 causal: rows see L-3, L-2, L-1, L positions
     assert v["flops"] == 16 * 128 * 2176 * (4 * 65536 - 6)
     assert np.isclose(v["intensity"], 128 * 2176 * (4 * 65536 - 6) / (65536 * 1152))
+
+
+def test_rank_shares_add_up_to_the_group():
+    # every position has exactly one owner, so the ranks' KV bytes and scores sum to
+    # the group's, for any interleave size
+    from workloads import configs as C
+    for w in C.ALL:
+        for I in (1, 16):
+            wi = C.scaled(w, interleave=I) if w.P % I == 0 else w
+            lens = np.array([1, 5, 777, 4096, 33333][: wi.B] + [100] * max(0, wi.B - 5))
+            tot = accounting.layer_step(wi, lens)
+            kv = sum(accounting.rank_share(wi, lens, r)["kv_bytes"] for r in range(wi.c))
+            fl = sum(accounting.rank_share(wi, lens, r)["flops"] for r in range(wi.c))
+            assert kv == tot["kv_bytes"] and fl == tot["flops"], (w.name, I)

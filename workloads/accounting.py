@@ -50,3 +50,29 @@ def layer_step(w: Workload, lens) -> dict:
                 decode_bytes=kv + w.c * q_bytes + part_bytes,
                 merge_bytes=part_bytes + final_bytes,
                 intensity=flops / kv if kv else 0.0)
+
+
+def owned_tokens(L: int, c: int, r: int, I: int = 1) -> int:
+    """Positions below L that rank r owns when runs of I positions go to the ranks in turn."""
+    full = L // (I * c)
+    return full * I + min(max(L - full * I * c - r * I, 0), I)
+
+
+def visible_scores_rank(w: Workload, lens, r: int) -> int:
+    """visible_scores restricted to the positions rank r owns."""
+    tot = 0
+    for L in np.asarray(lens, dtype=np.int64):
+        for i in range(w.q_len):
+            lim = int(L) - w.q_len + i + 1 if w.causal else int(L)
+            tot += owned_tokens(max(min(lim, int(L)), 0), w.c, r, w.interleave) * w.H
+    return tot
+
+
+def rank_share(w: Workload, lens, r: int = 0) -> dict:
+    """Algorithmic work of one rank's decode call (rank_begin = r, rank_count = 1):
+    the rank's KV rows read once, q read once, its partials written."""
+    lens = np.asarray(lens, dtype=np.int64)
+    kv = sum(owned_tokens(int(L), w.c, r, w.interleave) for L in lens) * kv_bytes_per_token(w)
+    rows = w.B * w.q_len * w.H
+    return dict(kv_bytes=kv, flops=visible_scores_rank(w, lens, r) * flops_per_score(),
+                decode_bytes=kv + rows * D_QK * 2 + rows * (D_V + 1) * 4)
