@@ -216,6 +216,33 @@ int mla_decode_partial(const dcp_layout* layout, const void* pools, const float*
                        int32_t* dev_status, hipStream_t stream);
 
 /*
+ * mla_decode_partial_noalloc - mla_decode_partial without a caller workspace.
+ *
+ * For callers that cannot allocate device memory at the call (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * work plan and the split partials go to a scratch array that the library
+ * holds in device memory (one copy per GPU, kept until the process ends, of
+ * mla_decode_noalloc_scratch_bytes() = 256 MiB); the call allocates and frees
+ * nothing.  Arguments, outputs and errors are those of mla_decode_partial,
+ * and the outputs are the same bit for bit; a call whose workspace size
+ * (mla_decode_workspace_size) exceeds the scratch returns DCP_ERR_WORKSPACE
+ * and enqueues nothing.  The scratch needs no clearing between calls (every
+ * call writes what it reads), but every call on one GPU shares it: calls that
+ * overlap in time on one GPU (several streams, or host threads) race and must
+ * be serialised by the caller.  DCP_ERR_HIP if the scratch address cannot be
+ * looked up on the current device.
+ */
+int mla_decode_partial_noalloc(const dcp_layout* layout, const void* pools, const float* pool_scales,
+                               int32_t rank_begin, int32_t rank_count, const void* q, int32_t batch,
+                               int32_t q_len, int32_t heads, const int32_t* block_table,
+                               int32_t bt_stride, const int32_t* seq_len, int64_t max_seq_len,
+                               float sm_scale, int32_t lse_base, int32_t causal, float* o_part,
+                               float* lse_part, int32_t* dev_status, hipStream_t stream);
+
+/* Bytes of the scratch array mla_decode_partial_noalloc uses (host call). */
+size_t mla_decode_noalloc_scratch_bytes(void);
+
+/*
  * dcp_lse_merge - exact merge of c partials (SGLang "Decode Context
  * Parallelism", section "MLA decode dataflow"): lse = logsumexp_r lse_r and
  * o = sum_r exp(lse_r - lse) * o_r, in base e or base 2 (the base of the

@@ -64,6 +64,9 @@ _SIGS = {
     "mla_decode_partial": (ctypes.c_int, [_PL, _VP, _VP, _I32, _I32, _VP, _I32, _I32, _I32, _VP, _I32, _VP,
                                           _I64, ctypes.c_float, _I32, _I32, _VP, _VP, _VP, ctypes.c_size_t,
                                           _VP, _VP]),
+    "mla_decode_partial_noalloc": (ctypes.c_int, [_PL, _VP, _VP, _I32, _I32, _VP, _I32, _I32, _I32, _VP, _I32,
+                                                  _VP, _I64, ctypes.c_float, _I32, _I32, _VP, _VP, _VP, _VP]),
+    "mla_decode_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "dcp_lse_merge": (ctypes.c_int, [_I32, _I64, _VP, _VP, _I32, _VP, _VP, _VP]),
     "dcp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -264,6 +267,33 @@ def mla_decode_partial(layout: Layout, pools, pool_scales, rank_begin: int, rank
         _ptr(lse_part, "lse_part", torch.float32, rank_count * rows), _ptr(workspace, "workspace"), ws_bytes,
         _ptr(dev_status, "dev_status", torch.int32, 1), _stream(stream))
     _check("mla_decode_partial", st)
+
+
+def mla_decode_partial_noalloc(layout: Layout, pools, pool_scales, rank_begin: int, rank_count: int, q,
+                               block_table, seq_len, max_seq_len: int, sm_scale: float, lse_base: int, causal: bool,
+                               o_part, lse_part, dev_status=None, stream=None):
+    """mla_decode_partial with the library's own scratch in place of a workspace."""
+    batch, q_len, heads, d = q.shape
+    if d != D_QK:
+        raise ValueError("q must be [batch][q_len][heads][576]")
+    rows = batch * q_len * heads
+    _need(0 <= rank_begin and rank_count >= 1 and rank_begin + rank_count <= layout.c, "ranks outside the group")
+    _pool_check(layout, pools, pool_scales, rank_count)
+    _table_rows(block_table, batch)
+    st = load_library().mla_decode_partial_noalloc(
+        ctypes.byref(layout), _ptr(pools, "pools", (torch.uint8, torch.int16, torch.bfloat16)),
+        _ptr(pool_scales, "pool_scales", torch.float32), rank_begin, rank_count,
+        _ptr(q, "q", (torch.bfloat16, torch.int16)), batch, q_len, heads,
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[-1],
+        _ptr(seq_len, "seq_len", torch.int32, batch), int(max_seq_len), float(sm_scale), int(lse_base),
+        1 if causal else 0, _ptr(o_part, "o_part", torch.float32, rank_count * rows * D_V),
+        _ptr(lse_part, "lse_part", torch.float32, rank_count * rows), _ptr(dev_status, "dev_status", torch.int32, 1),
+        _stream(stream))
+    _check("mla_decode_partial_noalloc", st)
+
+
+def mla_decode_noalloc_scratch_bytes() -> int:
+    return int(load_library().mla_decode_noalloc_scratch_bytes())
 
 
 def dcp_lse_merge(c: int, o_part, lse_part, lse_base: int, o_out, lse_out, stream=None):

@@ -27,6 +27,66 @@ int row_bytes(const dcp_layout* l) { return l->kv_dtype == DCP_KV_BF16 ? 2 * DCP
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DCP_OK : DCP_ERR_HIP; }
 
+// Argument checks shared by both decode entry points; on success fills the plan.
+int check_decode(const dcp_layout* layout, const void* pools, const float* pool_scales, int32_t rank_begin,
+                 int32_t rank_count, const void* q, int32_t batch, int32_t q_len, int32_t heads,
+                 const int32_t* block_table, int32_t bt_stride, const int32_t* seq_len, int64_t max_seq_len,
+                 float sm_scale, int32_t lse_base, const float* o_part, const float* lse_part, dcp::DecodePlan* pl) {
+  if (int s = check_layout(layout)) return s;
+  const bool fp8 = layout->kv_dtype == DCP_KV_FP8_E4M3;
+  if (rank_begin < 0 || rank_count < 1 || (int64_t)rank_begin + rank_count > layout->c) return DCP_ERR_INVALID_ARG;
+  if (batch < 0 || bt_stride < 1 || max_seq_len < 0) return DCP_ERR_INVALID_ARG;
+  if (lse_base != DCP_LSE_BASE_E && lse_base != DCP_LSE_BASE_2) return DCP_ERR_INVALID_ARG;
+  if (!isfinite(sm_scale)) return DCP_ERR_INVALID_ARG;
+  if (q_len < 1 || q_len > DCP_MAX_Q_LEN || heads < 16 || heads % 16 != 0 || heads > 4096)
+    return DCP_ERR_UNSUPPORTED;
+  if (max_seq_len > INT32_MAX) return DCP_ERR_UNSUPPORTED;
+  if (batch == 0) return DCP_OK;
+  if (!pools || !q || !block_table || !seq_len || !o_part || !lse_part) return DCP_ERR_INVALID_ARG;
+  if (fp8 && !pool_scales) return DCP_ERR_INVALID_ARG;
+  if (!aligned(pools, 16) || !aligned(q, 16) || !aligned(o_part, 16) || !aligned(lse_part, 4))
+    return DCP_ERR_ALIGNMENT;
+  if (fp8 && !aligned(pool_scales, 4)) return DCP_ERR_ALIGNMENT;
+  *pl = dcp::plan_decode(layout->c, interleave_of(layout), layout->page, fp8, rank_count, batch, q_len, heads,
+                         max_seq_len);
+  return DCP_OK;
+}
+
+int launch_decode_call(const dcp_layout* layout, const void* pools, const float* pool_scales, int32_t rank_begin,
+                       int32_t rank_count, const void* q, int32_t batch, int32_t q_len, int32_t heads,
+                       const int32_t* block_table, int32_t bt_stride, const int32_t* seq_len, int64_t max_seq_len,
+                       float sm_scale, int32_t lse_base, int32_t causal, float* o_part, float* lse_part,
+                       void* workspace, const dcp::DecodePlan& pl, int32_t* dev_status, hipStream_t stream) {
+  const bool fp8 = layout->kv_dtype == DCP_KV_FP8_E4M3;
+  dcp::DecodeArgs a{};
+  a.c = layout->c;
+  a.interleave = interleave_of(layout);
+  a.page = layout->page;
+  a.num_pages = layout->num_pages;
+  a.fp8 = fp8;
+  a.pools = pools;
+  a.pool_scales = pool_scales;
+  a.rank_begin = rank_begin;
+  a.rank_count = rank_count;
+  a.q = q;
+  a.batch = batch;
+  a.q_len = q_len;
+  a.heads = heads;
+  a.block_table = block_table;
+  a.bt_stride = bt_stride;
+  a.seq_len = seq_len;
+  a.max_seq_len = max_seq_len;
+  a.sm_scale = sm_scale;
+  a.base2 = lse_base == DCP_LSE_BASE_2;
+  a.causal = causal != 0;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.workspace = workspace;
+  a.dev_status = dev_status;
+  return hip_status(dcp::launch_decode(a, pl, stream));
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -122,54 +182,35 @@ int mla_decode_partial(const dcp_layout* layout, const void* pools, const float*
                        const int32_t* block_table, int32_t bt_stride, const int32_t* seq_len, int64_t max_seq_len,
                        float sm_scale, int32_t lse_base, int32_t causal, float* o_part, float* lse_part,
                        void* workspace, size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
-  if (int s = check_layout(layout)) return s;
-  const bool fp8 = layout->kv_dtype == DCP_KV_FP8_E4M3;
-  if (rank_begin < 0 || rank_count < 1 || (int64_t)rank_begin + rank_count > layout->c) return DCP_ERR_INVALID_ARG;
-  if (batch < 0 || bt_stride < 1 || max_seq_len < 0) return DCP_ERR_INVALID_ARG;
-  if (lse_base != DCP_LSE_BASE_E && lse_base != DCP_LSE_BASE_2) return DCP_ERR_INVALID_ARG;
-  if (!isfinite(sm_scale)) return DCP_ERR_INVALID_ARG;
-  if (q_len < 1 || q_len > DCP_MAX_Q_LEN || heads < 16 || heads % 16 != 0 || heads > 4096)
-    return DCP_ERR_UNSUPPORTED;
-  if (max_seq_len > INT32_MAX) return DCP_ERR_UNSUPPORTED;
-  if (batch == 0) return DCP_OK;
-  if (!pools || !q || !block_table || !seq_len || !o_part || !lse_part) return DCP_ERR_INVALID_ARG;
-  if (fp8 && !pool_scales) return DCP_ERR_INVALID_ARG;
-  if (!aligned(pools, 16) || !aligned(q, 16) || !aligned(o_part, 16) || !aligned(lse_part, 4))
-    return DCP_ERR_ALIGNMENT;
-  if (fp8 && !aligned(pool_scales, 4)) return DCP_ERR_ALIGNMENT;
-  dcp::DecodePlan pl = dcp::plan_decode(layout->c, interleave_of(layout), layout->page, fp8, rank_count, batch, q_len,
-                                        heads, max_seq_len);
-  if (pl.workspace_bytes > 0) {
-    if (!workspace || workspace_bytes < pl.workspace_bytes) return DCP_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return DCP_ERR_ALIGNMENT;
-  }
-  dcp::DecodeArgs a{};
-  a.c = layout->c;
-  a.interleave = interleave_of(layout);
-  a.page = layout->page;
-  a.num_pages = layout->num_pages;
-  a.fp8 = fp8;
-  a.pools = pools;
-  a.pool_scales = pool_scales;
-  a.rank_begin = rank_begin;
-  a.rank_count = rank_count;
-  a.q = q;
-  a.batch = batch;
-  a.q_len = q_len;
-  a.heads = heads;
-  a.block_table = block_table;
-  a.bt_stride = bt_stride;
-  a.seq_len = seq_len;
-  a.max_seq_len = max_seq_len;
-  a.sm_scale = sm_scale;
-  a.base2 = lse_base == DCP_LSE_BASE_2;
-  a.causal = causal != 0;
-  a.o_part = o_part;
-  a.lse_part = lse_part;
-  a.workspace = workspace;
-  a.dev_status = dev_status;
-  return hip_status(dcp::launch_decode(a, pl, stream));
+  dcp::DecodePlan pl{};
+  const int s = check_decode(layout, pools, pool_scales, rank_begin, rank_count, q, batch, q_len, heads, block_table,
+                             bt_stride, seq_len, max_seq_len, sm_scale, lse_base, o_part, lse_part, &pl);
+  if (s != DCP_OK || batch == 0) return s;
+  if (!workspace || workspace_bytes < pl.workspace_bytes) return DCP_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return DCP_ERR_ALIGNMENT;
+  return launch_decode_call(layout, pools, pool_scales, rank_begin, rank_count, q, batch, q_len, heads, block_table,
+                            bt_stride, seq_len, max_seq_len, sm_scale, lse_base, causal, o_part, lse_part, workspace,
+                            pl, dev_status, stream);
 }
+
+int mla_decode_partial_noalloc(const dcp_layout* layout, const void* pools, const float* pool_scales,
+                               int32_t rank_begin, int32_t rank_count, const void* q, int32_t batch, int32_t q_len,
+                               int32_t heads, const int32_t* block_table, int32_t bt_stride, const int32_t* seq_len,
+                               int64_t max_seq_len, float sm_scale, int32_t lse_base, int32_t causal, float* o_part,
+                               float* lse_part, int32_t* dev_status, hipStream_t stream) {
+  dcp::DecodePlan pl{};
+  const int s = check_decode(layout, pools, pool_scales, rank_begin, rank_count, q, batch, q_len, heads, block_table,
+                             bt_stride, seq_len, max_seq_len, sm_scale, lse_base, o_part, lse_part, &pl);
+  if (s != DCP_OK || batch == 0) return s;
+  if (pl.workspace_bytes > dcp::kScratchBytes) return DCP_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (dcp::decode_scratch(&ws) != hipSuccess) return DCP_ERR_HIP;
+  return launch_decode_call(layout, pools, pool_scales, rank_begin, rank_count, q, batch, q_len, heads, block_table,
+                            bt_stride, seq_len, max_seq_len, sm_scale, lse_base, causal, o_part, lse_part, ws, pl,
+                            dev_status, stream);
+}
+
+size_t mla_decode_noalloc_scratch_bytes(void) { return dcp::kScratchBytes; }
 
 int dcp_lse_merge(int32_t c, int64_t rows, const float* o_part, const float* lse_part, int32_t lse_base,
                   void* o_out, float* lse_out, hipStream_t stream) {

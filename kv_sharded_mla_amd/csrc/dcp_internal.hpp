@@ -77,6 +77,14 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 
+// Bytes of the file-scope scratch array the allocation-free decode entry
+// point uses instead of a caller's workspace.
+constexpr size_t kScratchBytes = (size_t)256 << 20;
+
+// Device address of that array on the current device (looked up once per
+// device; no allocation).
+hipError_t decode_scratch(void** ptr);
+
 int device_cu_count();
 
 }  // namespace dcp

@@ -29,6 +29,8 @@
 // the same result; probabilities stay below 2^kTau).
 // e4m3 KV: codes are converted exactly to bf16 for the MFMA, the per-token
 // scale multiplies the score and the probability that weights V.
+#include <mutex>
+
 #include "dcp_common.hpp"
 #include "dcp_internal.hpp"
 
@@ -1022,7 +1024,35 @@ hipError_t launch_pc(const DecodeParams& prm, bool aligned, int64_t grid, hipStr
   return hipGetLastError();
 }
 
+// Scratch of the allocation-free entry point: the work plan and the split
+// partials of one call, in a file-scope device array (one copy per GPU, held
+// until the process ends).  Host code never passes `scratch` itself to a
+// kernel (on the host it names a stand-in, not a device address): the device
+// address is looked up once per device with hipGetSymbolAddress.
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 int device_cu_count() {
   static int cached[64] = {0};
