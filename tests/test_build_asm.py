@@ -27,7 +27,8 @@ def asm(tmp_path_factory):
 
 def _kernels(asm):
     parts = re.split(r"\n(_ZN3dcp\w*mla_decode_(?:pc_)?kernel\w*):[^\n]*\n", asm)
-    return {parts[i]: parts[i + 1].split("s_endpgm")[0] for i in range(1, len(parts) - 1, 2)}
+    # a kernel's code runs to its .Lfunc_end label (early exits put s_endpgm inside)
+    return {parts[i]: parts[i + 1].split(".Lfunc_end")[0] for i in range(1, len(parts) - 1, 2)}
 
 
 def test_m0_only_feeds_lds_dma(asm):
@@ -55,14 +56,22 @@ def test_no_compiler_vmcnt_waits_inside_decode_loop(asm):
     # stages ahead.  A bf16 stage is 36 loads, 9 per consumer wave; an e4m3 stage is 18
     # loads (5 or 4 per wave) plus one scale load per wave.  A wait the compiler placed
     # for Q inside the loop would show up as a count such as 17, 16, ... 1.
-    # Waits before the first direct-to-LDS load (reading the work plan, Q and the page
-    # table) cannot interfere with the ring and are not checked.
+    # Waits before the first direct-to-LDS load (reading seq_len for the work plan, Q
+    # and the page table) cannot interfere with the ring and are not checked.
     allowed = {0} | {k * n for n in (5, 6, 9) for k in range(1, 8)}
     for name, body in _kernels(asm).items():
         first_dma = body.find("global_load_lds")
         assert first_dma > 0, name
         waits = set(int(x) for x in re.findall(r"vmcnt\((\d+)\)", body[first_dma:]))
         assert waits <= allowed, (name, sorted(waits))
+
+
+def test_no_scalar_stores_or_atomics(asm):
+    # memory is written only through vector stores and vector atomics
+    for name, body in _kernels(asm).items():
+        bad = re.findall(r"^\s*(s_store\w*|s_buffer_store\w*|s_atomic\w*|s_buffer_atomic\w*|s_dcache_wb\w*|s_scratch_store\w*)",
+                         body, re.M)
+        assert not bad, (name, bad[:4])
 
 
 def test_non_temporal_loads_only_in_single_row_block_kernels(asm):

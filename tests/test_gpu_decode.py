@@ -230,3 +230,36 @@ def test_rank_subset_calls(name, w, lens, short):
             # arithmetic in either call: bit for bit
             assert np.array_equal(o_p.view(np.uint32), o_full[rb:rb + rc].view(np.uint32))
             assert np.array_equal(l_p.view(np.uint32), l_full[rb:rb + rc].view(np.uint32))
+
+
+@pytest.mark.parametrize("fill", ["all_bits_set", "random_bytes"])
+def test_workspace_contents_do_not_matter(fill):
+    # Every call writes the workspace parts it reads (work plan, split
+    # partials): a workspace left full of other data (every bit set, or random
+    # bytes) gives the outputs of a zeroed one, bit for bit, on each of several
+    # calls in a row, and those match the oracle.  Ragged lengths (split and
+    # single-item units, an empty rank) and 64-row blocks (two per request)
+    # on bf16 and e4m3.
+    import torch
+    from kv_sharded_mla_amd import LSE_BASE_E
+    for kv in ("bf16", "fp8"):
+        w = W(index=110, H=128, c=4, P=64, B=3, kv_dtype=kv)
+        case = Case(w, lens=[30000, 9000, 3])
+        ws0 = case.group.workspace_for(w.q_len, w.H)
+        ws0.zero_()
+        ref_o, ref_l = case.group.decode(case.q, w.sm_scale, LSE_BASE_E, w.causal, workspace=ws0)
+        ref_o, ref_l = ref_o.clone(), ref_l.clone()
+        ws = torch.empty_like(ws0)
+        if fill == "all_bits_set":
+            ws.view(torch.int32).fill_(-1)
+        else:
+            g = torch.Generator(device="cuda").manual_seed(7)
+            ws.view(torch.int32).copy_(torch.randint(-2**31, 2**31 - 1, ws.shape, generator=g, device="cuda",
+                                                     dtype=torch.int64).to(torch.int32))
+        for k in range(3):
+            o, l = case.group.decode(case.q, w.sm_scale, LSE_BASE_E, w.causal, workspace=ws)
+            torch.cuda.synchronize()
+            log(f"{kv} {fill} call {k}: identical={bool(torch.equal(o, ref_o) and torch.equal(l, ref_l))}")
+            assert torch.equal(o, ref_o) and torch.equal(l, ref_l), (kv, fill, k)
+        assert case.group.status() == 0
+        check_case(case)
