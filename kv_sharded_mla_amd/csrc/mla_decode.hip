@@ -899,38 +899,51 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   }
 }
 
-// Merge of the base-2 partials [0, n) of one row over columns 8t..8t+7, all
-// weighted against their own maximum: acc = sum_r 2^(l_r - m) o_r / tot and
-// lse = m + log2 tot; no partial (or only empty ones): lse = -inf, acc = 0.
-// The partials are loaded 8 at a time before they are combined.
+// Merge of the base-2 partials [0, n) of one row over columns 8t..8t+7:
+// acc = sum_r 2^(l_r - m) o_r / tot and lse = m + log2 tot with m the largest
+// l_r; no partial (or only empty ones): lse = -inf, acc = 0.  One pass over the
+// partials, 8 at a time (their lse and columns loaded together, then the
+// running maximum and sums rescaled as in the online softmax), so a pair
+// costs one round of load latency per 8 partials.
 __device__ __forceinline__ void merge_cols8(const float* __restrict__ o, int64_t o_stride,
                                             const float* __restrict__ lse, int64_t lse_stride, int n, int t,
                                             f32x4& a0, f32x4& a1, float& lse_out) {
-  float m = -INFINITY;
-  for (int r = 0; r < n; ++r) m = fmaxf(m, lse[r * lse_stride]);
+  float m = -INFINITY, tot = 0.f;
   a0 = f32x4{0.f, 0.f, 0.f, 0.f};
   a1 = a0;
-  lse_out = -INFINITY;
-  if (m == -INFINITY) return;
-  float tot = 0.f;
   for (int r0 = 0; r0 < n; r0 += 8) {
     float l[8];
     f32x4 v0[8], v1[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < 8; ++k) {
+      l[k] = -INFINITY;
       if (r0 + k < n) {
         l[k] = lse[(r0 + k) * lse_stride];
         v0[k] = *reinterpret_cast<const f32x4*>(o + (r0 + k) * o_stride + 8 * t);
         v1[k] = *reinterpret_cast<const f32x4*>(o + (r0 + k) * o_stride + 8 * t + 4);
       }
+    }
+    float mb = m;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mb = fmaxf(mb, l[k]);
+    if (mb == -INFINITY) continue;
+    const float sc = exp2f(m - mb);  // 0 while nothing was summed (m = -inf)
+    tot *= sc;
+    a0 *= sc;
+    a1 *= sc;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      if (r0 + k < n && l[k] != -INFINITY) {
-        const float w = exp2f(l[k] - m);
+      if (l[k] != -INFINITY) {
+        const float w = exp2f(l[k] - mb);
         tot += w;
         a0 += w * v0[k];
         a1 += w * v1[k];
       }
+    m = mb;
+  }
+  if (m == -INFINITY) {
+    lse_out = -INFINITY;
+    return;
   }
   const float inv = 1.0f / tot;
   a0 *= inv;
@@ -938,15 +951,6 @@ __device__ __forceinline__ void merge_cols8(const float* __restrict__ o, int64_t
   lse_out = m + log2f(tot);
 }
 
-// Merge the items of every split unit, row by row: partials (lse in base 2)
-// -> o_part, lse_part in the requested base.  Units with one item were
-// written directly by the decode kernel.  With fewer than 8 items in every
-// unit, each 64-thread group of a 256-thread workgroup merges one (split
-// unit, row) pair (8 columns per thread), grid-stride.  Otherwise a
-// workgroup takes one pair at a time: each of its four groups merges a
-// quarter of the unit's items and the first group merges the four results
-// (the same log-sum-exp merge, so long runs of items are not one serial
-// chain of loads).
 __global__ void __launch_bounds__(256) split_combine_kernel(DecodeParams p) {
   __shared__ float s_lse[4];
   __shared__ f32x4 s_acc[4][64][2];
