@@ -10,10 +10,10 @@
 // block table is the rank-local page table.
 //
 // Kernel shape.  A workgroup of 8 waves owns one (rank, request, KV split,
-// block of 16*RGN query rows).  KV is streamed through an LDS ring of
-// 32-token stages filled by direct-to-LDS 16-byte loads
+// block of 16*RGN query rows).  KV is streamed through an LDS ring of 36 KB
+// stages (32 bf16 or 64 e4m3 tokens) filled by direct-to-LDS 16-byte loads
 // (global_load_lds_dwordx4); every latent row is read from HBM once per
-// workgroup and serves all of its query rows:
+// workgroup and serves all of its query rows.  Per 32 tokens:
 //   S^T[32 tok x 16 rows] = K[32 x 576] . Q^T           (mfma 16x16x32 bf16, K from LDS,
 //                                                       Q^T held in registers)
 //   O^T[512 x 16 rows]   += V^T[512 x 32] . P^T         (V^T read from the same LDS rows
@@ -44,7 +44,7 @@ constexpr int kWaves = 8;     // waves per workgroup: two per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr float kTau = 8.0f;
 constexpr int kMaxTab = 512;  // page ids staged per workgroup
-constexpr int kStageTok = 32; // tokens per LDS stage
+constexpr int kStageTok = 32; // tokens per LDS stage, bf16 KV (e4m3 KV: 64, the same bytes)
 constexpr int kCombineBlocksPerCu = 8;  // split-combine workgroups per CU (grid-stride beyond)
 constexpr int kItemMinStages = 8;       // shortest work item (each pays a q load and a partial write)
 constexpr int kItemsPerCu = 2;          // work items the plan aims for per CU and row block
@@ -67,6 +67,7 @@ struct DecodeParams {
   float* o_part;    // [units][rows][512], unit = rank * batch + request
   float* lse_part;  // [units][rows]
   int32_t n_row_blocks;
+  int32_t stage_tok;  // tokens per LDS stage (and the plan's unit of work)
   int32_t units;    // rank_count * batch
   int32_t direct;   // every unit is one item: no work plan, item i = unit i
   // work plan (written each call by decode_plan_kernel, in the workspace)
@@ -266,9 +267,9 @@ __device__ __forceinline__ int32_t visible_tokens(int32_t L, int32_t r, int32_t 
 
 // Decode kernel: a workgroup of 8 waves owns RGN row blocks of 16 query rows
 // (RGN = 4, 2 or 1).  Waves 0..RGN-1 produce: wave q owns row block q,
-// computes its full S^T (both 16-token blocks, all 576 columns), the online
-// softmax and P^T, and publishes P^T (with the rescale factors when the
-// running maximum moved) in a double-buffered LDS area.  Waves 4-7 consume:
+// computes its full S^T (every 16-token block of the tile, all 576 columns),
+// the online softmax and P^T, and publishes P^T (with the rescale factors
+// when the running maximum moved) in a double-buffered LDS area.  Waves 4-7 consume:
 // wave 4+c owns output columns [128c, 128c+128) of every row block and
 // multiplies V^T by the P^T of the previous tile, so each transposed V
 // fragment feeds RGN MFMAs; waves RGN..3 (RGN < 4) only take part in the
@@ -285,20 +286,26 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   constexpr int MB = 16 * RGN;            // query rows per workgroup
   constexpr int ROWB = FP8 ? kDqk : 2 * kDqk;
   constexpr int CH = ROWB / 16;
-  constexpr int STOK = 32;                // tokens per stage (one tile)
-  constexpr int SBYTES = STOK * ROWB;     // 36864 (bf16) or 18432 (e4m3)
-  constexpr int NSTG = FP8 ? 8 : 4;       // ring stages
+  // tokens per stage (one tile): a 36 KB stage either way, 32 bf16 or 64
+  // e4m3 rows, so an e4m3 tile carries the bytes of a bf16 one for the same
+  // per-tile costs (barrier, softmax reductions, flags)
+  constexpr int STOK = FP8 ? 64 : 32;
+  constexpr int NTB = STOK / 16;          // 16-token blocks of a tile (score MFMA rows)
+  constexpr int NH = STOK / 32;           // 32-token halves of a tile (PV MFMA k-steps)
+  constexpr int SBYTES = STOK * ROWB;     // 36864
+  constexpr int NSTG = FP8 ? 3 : 4;       // ring stages
   constexpr int NI_ALL = SBYTES / 1024;   // 1 KB direct-to-LDS loads per stage
   constexpr int NLW = 4;                  // loading (consumer) waves
   constexpr int NI_MAX = (NI_ALL + NLW - 1) / NLW;            // loads of the busiest loading wave
   constexpr int NBIG = NI_ALL % NLW == 0 ? NLW : NI_ALL % NLW;  // loading waves that issue NI_MAX
   constexpr int NDBC = 8;                 // output blocks per consumer wave
+  constexpr int SCW = STOK / NLW;         // e4m3 token scales loaded per loading wave
   constexpr int KU = FP8 ? 9 : 18;        // k units (k-steps, or e4m3 k-step pairs)
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds_kv[NSTG * SBYTES];
   __shared__ __attribute__((aligned(16))) float lds_sc[FP8 ? NSTG * STOK : 4];
   __shared__ int32_t lds_pt[kMaxTab];
-  __shared__ __attribute__((aligned(16))) bf16x8 lds_p[2][RGN * 64];
+  __shared__ __attribute__((aligned(16))) bf16x8 lds_p[2][RGN * NH * 64];
   __shared__ float lds_alpha[2][RGN * 16];
   __shared__ __attribute__((aligned(16))) int lds_resc[2][4];  // read as one 16-byte vector
   __shared__ float lds_l[RGN * 16];
@@ -421,7 +428,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
 #pragma unroll
       for (int t = 0; t < NI_MAX; ++t)
         if (t < ni) dma16<NT>(base, dma_off[t], dst + (lw + NLW * t) * 1024);
-      if (FP8 && lane < 8) dma4_abs<NT>(spool + slot0 + 8 * lw + lane, dst_sc + 8 * lw);
+      if (FP8 && lane < SCW) dma4_abs<NT>(spool + slot0 + SCW * lw + lane, dst_sc + SCW * lw);
     } else {
       // last stage of a split (rows past j_end repeat the last valid row) or
       // pages that a stage can straddle
@@ -432,14 +439,16 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
           dma16_abs<NT>(pool + slot_of(jj) * ROWB + (dma_off[t] - dma_row[t] * ROWB), dst + (lw + NLW * t) * 1024);
         }
       if (FP8) {
-        const int32_t jj = min(j0 + 8 * lw + (lane & 7), j_end - 1);
+        const int32_t jj = min(j0 + SCW * lw + (lane & (SCW - 1)), j_end - 1);
         const float* src = spool + slot_of(jj);
-        if (lane < 8) dma4_abs<NT>(src, dst_sc + 8 * lw);
+        if (lane < SCW) dma4_abs<NT>(src, dst_sc + SCW * lw);
       }
     }
   };
 
-  // producer K offsets (both token blocks) and consumer V^T offsets
+  // producer K offsets (token blocks 0 and 1) and consumer V^T offsets (the
+  // first 32 tokens); the swizzles leave row bit 5 alone, so token block
+  // tb + 2 and the second half of a 64-token tile sit 32 rows further
   int koff[2][2], voff[2][4];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
@@ -473,14 +482,16 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     const uint8_t* kv = lds_kv + (t % NSTG) * SBYTES;
     const float* sc = lds_sc + (FP8 ? (t % NSTG) * STOK : 0);
     const int32_t jt = j_begin + tile_of(t) * STOK;
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    // e4m3 token scales of this lane's 8 tokens, read before the score
-    // MFMAs so that their LDS latency is hidden
-    float tsc[8];
+    f32x4 sacc[NTB];
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) sacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // e4m3 token scales of this lane's tokens, read before the score MFMAs
+    // so that their LDS latency is hidden
+    float tsc[4 * NTB];
     if (FP8) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // token 16h + 4g + i of the stage: one 16-byte read per half (the 16
+      for (int h = 0; h < NTB; ++h) {
+        // token 16h + 4g + i of the stage: one 16-byte read per block (the 16
         // lanes of a row group read the same four scales)
         const f32x4 v = *reinterpret_cast<const f32x4*>(sc + 16 * h + 4 * g);
 #pragma unroll
@@ -490,13 +501,15 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     // K fragments f = 2u + tb (k unit u, token block tb), kept PD loads ahead
     // of the MFMA that uses them; the schedule below pins that interleave.
     if (FP8) {
-      constexpr int NF = 2 * KU, PD = 6;
+      constexpr int NF = NTB * KU, PD = 6;
       i32x4 kf[NF];
       // fragment f: k unit u of token block tb, token-block major (each
       // accumulator takes its MFMAs back to back)
       auto ftb = [](int f) { return f / KU; };
       auto fu = [](int f) { return f % KU; };
-      auto kload = [&](int f) { return *reinterpret_cast<const i32x4*>(kv + koff[ftb(f)][0] + 64 * fu(f)); };
+      auto kload = [&](int f) {
+        return *reinterpret_cast<const i32x4*>(kv + koff[ftb(f) & 1][0] + (ftb(f) >> 1) * 32 * ROWB + 64 * fu(f));
+      };
 #pragma unroll
       for (int f = 0; f < PD; ++f) kf[f] = kload(f);
 #pragma unroll
@@ -543,9 +556,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     // is detected with a ballot and only then is the row maximum formed
     // across the lanes of the row.  exp2 is the hardware instruction: a
     // probability below 2^-126 flushes to zero, far below what bf16 P keeps.
-    float y[8];
+    constexpr int NY = 4 * NTB;
+    float y[NY];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NY; ++e) {
       y[e] = sacc[e >> 2][e & 3];
       if (FP8) y[e] *= tsc[e];
       y[e] *= p.scale_log2;
@@ -554,10 +568,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
       // masked by adding -inf, so every y stays an arithmetic result (the max
       // below then needs no NaN canonicalisation)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+      for (int e = 0; e < NY; ++e)
         y[e] += (jt + (e >> 2) * 16 + 4 * g + (e & 3) >= jlim_s) ? -INFINITY : 0.f;
     }
     float mloc = max3f(max3f(y[0], y[1], y[2]), max3f(y[3], y[4], y[5]), fmaxf(y[6], y[7]));
+#pragma unroll
+    for (int e = 8; e < NY; e += 8)
+      mloc = max3f(mloc, max3f(y[e], y[e + 1], y[e + 2]), max3f(max3f(y[e + 3], y[e + 4], y[e + 5]), y[e + 6], y[e + 7]));
     float alpha = 1.f;
     const bool resc = __any(mloc > m_run + kTau);
     if (resc) {
@@ -569,16 +586,18 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     }
     const float mref = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
-    bf16x8 pf;
+    // P^T of 32-token half h: token blocks 2h and 2h + 1 (the PV operand order)
+    bf16x8 pf[NH];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NY; ++e) {
       float pe = __builtin_amdgcn_exp2f(y[e] - mref);
       psum += pe;
       if (FP8) pe *= tsc[e];
-      pf[e] = (__bf16)pe;
+      pf[e >> 3][e & 7] = (__bf16)pe;
     }
     l_run = l_run * alpha + psum;
-    lds_p[t & 1][rbq * 64 + lane] = pf;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) lds_p[t & 1][(rbq * NH + h) * 64 + lane] = pf[h];
     if (resc) {
       if (g == 0) lds_alpha[t & 1][rbq * 16 + j] = alpha;
       if (lane == 0) lds_resc[t & 1][rbq] = t;
@@ -587,28 +606,39 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
 
   auto consume = [&](int t) {
     const uint8_t* kv = lds_kv + (t % NSTG) * SBYTES;
-    // every LDS read of the tile is issued first: the rescale flags, P^T of
-    // the four row blocks and the eight V^T fragments; the MFMAs then wait
-    // for them in issue order
-    const i32x4 resc = *reinterpret_cast<const i32x4*>(&lds_resc[t & 1][0]);
-    bf16x8 pg[RGN];
+    // P^T of the row blocks and the eight V^T fragments of 32-token half h
+    bf16x8 pg[RGN], vf[NDBC];
+    auto operands = [&](int h) {
 #pragma unroll
-    for (int q = 0; q < RGN; ++q) pg[q] = lds_p[t & 1][q * 64 + lane];
-    bf16x8 vf[NDBC];
+      for (int q = 0; q < RGN; ++q) pg[q] = lds_p[t & 1][(q * NH + h) * 64 + lane];
 #pragma unroll
-    for (int d = 0; d < NDBC; ++d) {
-      const int db = cq * NDBC + d;
-      if (FP8) {
-        i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(DCP_LDS(i32x2, kv + voff[0][db & 3] + 64 * (db >> 2)));
-        vf[d] = cvt_fp8x8(raw);
-      } else {
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DCP_LDS(i16x4, kv + voff[0][db & 3] + 128 * (db >> 2)));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DCP_LDS(i16x4, kv + voff[1][db & 3] + 128 * (db >> 2)));
-        typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
-        i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        vf[d] = __builtin_bit_cast(bf16x8, v);
+      for (int d = 0; d < NDBC; ++d) {
+        const int db = cq * NDBC + d;
+        if (FP8) {
+          i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              DCP_LDS(i32x2, kv + voff[0][db & 3] + 64 * (db >> 2) + h * 32 * ROWB));
+          vf[d] = cvt_fp8x8(raw);
+        } else {
+          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DCP_LDS(i16x4, kv + voff[0][db & 3] + 128 * (db >> 2)));
+          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DCP_LDS(i16x4, kv + voff[1][db & 3] + 128 * (db >> 2)));
+          typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+          i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          vf[d] = __builtin_bit_cast(bf16x8, v);
+        }
       }
-    }
+    };
+    auto mfmas = [&]() {
+#pragma unroll
+      for (int d = 0; d < NDBC; ++d)
+#pragma unroll
+        for (int q = 0; q < RGN; ++q)
+          R[d * RGN + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], pg[q], R[d * RGN + q], 0, 0, 0);
+    };
+    // every LDS read of the first half is issued first (the rescale flags,
+    // P^T and V^T); the rescale and the MFMAs then wait for them in issue
+    // order
+    const i32x4 resc = *reinterpret_cast<const i32x4*>(&lds_resc[t & 1][0]);
+    operands(0);
     bool any_resc = false;
 #pragma unroll
     for (int q = 0; q < RGN; ++q) any_resc |= resc[q] == t;
@@ -621,11 +651,12 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
           for (int d = 0; d < NDBC; ++d) R[d * RGN + q] *= a;
         }
     }
+    mfmas();
 #pragma unroll
-    for (int d = 0; d < NDBC; ++d)
-#pragma unroll
-      for (int q = 0; q < RGN; ++q)
-        R[d * RGN + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], pg[q], R[d * RGN + q], 0, 0, 0);
+    for (int h = 1; h < NH; ++h) {
+      operands(h);
+      mfmas();
+    }
   };
 
   // stages 0 .. NSTG-2 in flight; stage 0 resident before the first tile
@@ -786,7 +817,7 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     const int b = u % p.batch, rl = u / p.batch;
     const int32_t L = request_len(p, b, false);
     const int32_t n = visible_tokens(L, p.rank_begin + rl, p.c, p.interleave, p.q_len, p.q_len - 1, p.causal);
-    return (n + kStageTok - 1) / kStageTok;
+    return (n + p.stage_tok - 1) / p.stage_tok;
   };
   // the first chunk's stage counts stay in a register (one read of seq_len)
   const int32_t st0 = tid < p.units ? unit_stages(tid) : 0;
@@ -882,8 +913,8 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
       p.unit_count[u] = items;
       for (int32_t k = 0; k < items; ++k) {
         p.item_unit[first + k] = u;
-        p.item_jb[first + k] = k * len * kStageTok;
-        p.item_je[first + k] = min((k + 1) * len, st) * kStageTok;
+        p.item_jb[first + k] = k * len * p.stage_tok;
+        p.item_je[first + k] = min((k + 1) * len, st) * p.stage_tok;
       }
       if (items > 1) p.split_units[nsplit] = u;
     }
@@ -1072,20 +1103,22 @@ int device_cu_count() {
 
 DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, int32_t rank_count, int32_t batch,
                        int32_t q_len, int32_t heads, int64_t max_seq_len) {
-  (void)fp8;
+
   DecodePlan pl{};
   pl.rows = q_len * heads;
   const int rg = pl.rows % 64 == 0 ? 4 : (pl.rows % 32 == 0 ? 2 : 1);
   pl.row_block = 16 * rg;
   pl.n_row_blocks = pl.rows / pl.row_block;
-  pl.stage_tokens = kStageTok;
+  pl.stage_tokens = fp8 ? 2 * kStageTok : kStageTok;
+  const int32_t stok = pl.stage_tokens;
   pl.units = (int64_t)rank_count * batch;
   // a rank owns at most ceil(L / (I c)) chunks of I positions of a request of L
   const int64_t cyc = (int64_t)interleave * c;
   const int64_t n_r_max = (max_seq_len + cyc - 1) / cyc * interleave;
-  const int64_t stages_max = (n_r_max + kStageTok - 1) / kStageTok;
-  pl.t_max = (int32_t)std::max<int64_t>(1, (int64_t)(kMaxTab - 1) * page / kStageTok);
-  pl.t_min = std::min<int32_t>(kItemMinStages, pl.t_max);
+  const int64_t stages_max = (n_r_max + stok - 1) / stok;
+  pl.t_max = (int32_t)std::max<int64_t>(1, (int64_t)(kMaxTab - 1) * page / stok);
+  // the shortest item: kItemMinStages 32-token stages' worth of tokens
+  pl.t_min = std::min<int32_t>(std::max<int32_t>(1, kItemMinStages * kStageTok / stok), pl.t_max);
   pl.items_target = std::max<int32_t>(1, kItemsPerCu * device_cu_count() / pl.n_row_blocks);
   // the device plan makes at most units + max(items_target, units * ceil(stages_max / t_max)) items;
   // the item length T is at least t_min stages, so a unit of at most t_min
@@ -1139,6 +1172,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   prm.o_part = a.o_part;
   prm.lse_part = a.lse_part;
   prm.n_row_blocks = pl.n_row_blocks;
+  prm.stage_tok = pl.stage_tokens;
   prm.units = (int32_t)pl.units;
   prm.max_items = (int32_t)pl.max_items;
   prm.items_target = pl.items_target;
@@ -1165,7 +1199,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const bool aligned = a.page % kStageTok == 0;
+  const bool aligned = a.page % pl.stage_tokens == 0;
   const int64_t grid = (pl.max_items + 7) / 8 * 8 * pl.n_row_blocks;
   const int rg = pl.row_block / 16;
   if (a.fp8)
