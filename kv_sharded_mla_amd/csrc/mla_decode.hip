@@ -9,8 +9,8 @@
 // = floor(j/P) and floor(((jc+r) mod Pc)/c) = j mod P for r < c: the shared
 // block table is the rank-local page table.
 //
-// Kernel shape.  A workgroup of 8 waves owns one (rank, request, KV split,
-// block of 16*RGN query rows).  KV is streamed through an LDS ring of 36 KB
+// Kernel shape.  A workgroup of 8 waves (16 for 64-row bf16 blocks) owns one
+// (rank, request, KV split, block of 16*RGN query rows).  KV is streamed through an LDS ring of 36 KB
 // stages (32 bf16 or 64 e4m3 tokens) filled by direct-to-LDS 16-byte loads
 // (global_load_lds_dwordx4); every latent row is read from HBM once per
 // workgroup and serves all of its query rows.  Per 32 tokens:
@@ -40,8 +40,6 @@ namespace dcp {
 
 namespace {
 
-constexpr int kWaves = 8;     // waves per workgroup: two per SIMD
-constexpr int kThreads = kWaves * 64;
 constexpr float kTau = 8.0f;
 constexpr int kMaxTab = 512;  // page ids staged per workgroup
 constexpr int kStageTok = 32; // tokens per LDS stage, bf16 KV (e4m3 KV: 64, the same bytes)
@@ -265,23 +263,39 @@ __device__ __forceinline__ int32_t visible_tokens(int32_t L, int32_t r, int32_t 
   return owned_below((lim + 1 < L ? lim + 1 : L), r, c, il);
 }
 
-// Decode kernel: a workgroup of 8 waves owns RGN row blocks of 16 query rows
-// (RGN = 4, 2 or 1).  Waves 0..RGN-1 produce: wave q owns row block q,
-// computes its full S^T (every 16-token block of the tile, all 576 columns),
-// the online softmax and P^T, and publishes P^T (with the rescale factors
-// when the running maximum moved) in a double-buffered LDS area.  Waves 4-7 consume:
-// wave 4+c owns output columns [128c, 128c+128) of every row block and
-// multiplies V^T by the P^T of the previous tile, so each transposed V
-// fragment feeds RGN MFMAs; waves RGN..3 (RGN < 4) only take part in the
-// barriers.  One
-// workgroup barrier per tile hands P^T over and recycles the stage the
-// consumers finished; producer and consumer of a SIMD run different phases
+// Decode kernel: a workgroup owns RGN row blocks of 16 query rows (RGN = 4,
+// 2 or 1).  Waves 0..RGN-1 produce: wave q owns row block q, computes its
+// full S^T (every 16-token block of the tile, all 576 columns), the online
+// softmax and P^T, and publishes P^T (with the rescale factors when the
+// running maximum moved) in a double-buffered LDS area.  The consumers
+// multiply V^T by the P^T of the previous tile for a slice of the 512 output
+// columns of every row block, so each transposed V fragment feeds RGN MFMAs.
+// One workgroup barrier per tile hands P^T over and recycles the stage the
+// consumers finished; producer and consumers of a SIMD run different phases
 // and overlap (all waves at the same priority: a raised producer priority
-// measured 3-4% slower).  The consumers issue every direct-to-LDS load,
-// which keeps the producers' path from one barrier to the next free of load
-// issue and waits.
+// measured 3-4% slower).  Two shapes:
+// * 8 waves (two per SIMD, up to 256 registers each): waves 4-7 consume,
+//   wave 4+c owning columns [128c, 128c+128), and also issue every
+//   direct-to-LDS load, which keeps the producers' path from one barrier to
+//   the next free of load issue and waits; waves RGN..3 (RGN < 4) only take
+//   part in the barriers;
+// * 16 waves for bf16 blocks of 64 rows (four per SIMD, at most 128
+//   registers each): waves 4-11 consume, wave 4+c owning columns
+//   [64c, 64c+64), and waves 12-15 only issue the loads.  Issuing a stage's
+//   loads holds the issuing wave for most of a tile; here no wave that
+//   computes is held (128-head workloads 5-7% faster than with 8 waves).  The
+//   e4m3 producer does not fit 128 registers with 64-token tiles, and 32-token
+//   e4m3 tiles with loader waves measured slower than 8 waves with 64-token
+//   tiles.
+template <int RGN, bool FP8>
+constexpr bool kLoaderWaves = RGN == 4 && !FP8;
+template <int RGN, bool FP8>
+constexpr int kPcThreads = kLoaderWaves<RGN, FP8> ? 1024 : 512;
+
 template <int RGN, bool FP8, bool ALIGNED, bool NT>
-__global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams p) {
+__global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kernel(DecodeParams p) {
+  constexpr bool LDW = kLoaderWaves<RGN, FP8>;
+  constexpr int NTHR = kPcThreads<RGN, FP8>;
   static_assert(RGN == 1 || RGN == 2 || RGN == 4, "row blocks per workgroup");
   constexpr int MB = 16 * RGN;            // query rows per workgroup
   constexpr int ROWB = FP8 ? kDqk : 2 * kDqk;
@@ -295,10 +309,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   constexpr int SBYTES = STOK * ROWB;     // 36864
   constexpr int NSTG = FP8 ? 3 : 4;       // ring stages
   constexpr int NI_ALL = SBYTES / 1024;   // 1 KB direct-to-LDS loads per stage
-  constexpr int NLW = 4;                  // loading (consumer) waves
+  constexpr int NLW = 4;                  // waves that issue the direct-to-LDS loads
   constexpr int NI_MAX = (NI_ALL + NLW - 1) / NLW;            // loads of the busiest loading wave
   constexpr int NBIG = NI_ALL % NLW == 0 ? NLW : NI_ALL % NLW;  // loading waves that issue NI_MAX
-  constexpr int NDBC = 8;                 // output blocks per consumer wave
+  constexpr int NDBC = LDW ? 4 : 8;       // output blocks per consumer wave
   constexpr int SCW = STOK / NLW;         // e4m3 token scales loaded per loading wave
   constexpr int KU = FP8 ? 9 : 18;        // k units (k-steps, or e4m3 k-step pairs)
 
@@ -314,9 +328,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   const int w = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, j = lane & 15;
   const bool producer = w < RGN;
-  const bool consumer = w >= 4;           // waves RGN..3 (RGN < 4) only join the barriers
+  const bool consumer = LDW ? (w >= 4 && w < 12) : w >= 4;
+  const bool loader = LDW ? w >= 12 : w >= 4;  // with 8 waves the consumers load
   const int rbq = w & 3;                  // producer: its row block
-  const int cq = w & 3;                   // consumer: its column group
+  const int cq = LDW ? w - 4 : (w & 3);   // consumer: its column group
 
   const WgUnit wu = wg_unit(blockIdx.x, p.n_row_blocks);
   const int rb = wu.rb;
@@ -360,7 +375,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   const int32_t n_tab = n_st > 0 ? (j_end - 1) / Pi - vp_first + 1 : 0;
   {
     bool bad_page = false;
-    for (int t = tid; t < n_tab; t += kThreads) {
+    for (int t = tid; t < n_tab; t += NTHR) {
       int32_t pg = bt[vp_first + t];
       if ((unsigned)pg >= (unsigned)p.num_pages) {
         bad_page = true;
@@ -374,7 +389,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
 
   // One register array serves both roles, which are fixed per wave: a
   // producer keeps its Q^T fragments (18 x 16 bytes) in R[0..17], a consumer
-  // its O^T accumulators (8 blocks x 4 row blocks) in R[0..31].
+  // its O^T accumulators (NDBC column blocks x RGN row blocks).
   constexpr int NR = NDBC * RGN > 18 ? NDBC * RGN : 18;
   f32x4 R[NR];
   if (producer) {
@@ -395,21 +410,23 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   wait_vmcnt<0>();
   __syncthreads();
 
-  // direct-to-LDS loads, issued by the consumer waves: loading wave lw issues
+  // direct-to-LDS loads, issued by the loading waves: loading wave lw issues
   // loads lw, lw + 4, ... of a stage; load i fills LDS bytes [1024 i, 1024 i +
   // 1024), lane k the 16 bytes at 1024 i + 16 k, which hold chunk
   // (pos ^ swz(row)) of stage row `row` (pos = position inside the row)
   const int lw = w & 3;
-  const int ni = consumer ? (lw < NBIG ? NI_MAX : NI_MAX - 1) : 0;
+  const int ni = loader ? (lw < NBIG ? NI_MAX : NI_MAX - 1) : 0;
   int dma_row[NI_MAX];
   uint32_t dma_off[NI_MAX];
+  auto init_dma = [&]() {
 #pragma unroll
-  for (int t = 0; t < NI_MAX; ++t) {
-    const int ci = (lw + NLW * t) * 64 + lane;
-    const int row = min(ci / CH, STOK - 1);
-    dma_row[t] = row;
-    dma_off[t] = (uint32_t)(row * ROWB + ((ci % CH) ^ swz<FP8>(row)) * 16);
-  }
+    for (int t = 0; t < NI_MAX; ++t) {
+      const int ci = (lw + NLW * t) * 64 + lane;
+      const int row = min(ci / CH, STOK - 1);
+      dma_row[t] = row;
+      dma_off[t] = (uint32_t)(row * ROWB + ((ci % CH) ^ swz<FP8>(row)) * 16);
+    }
+  };
   auto slot_of = [&](int32_t jj) -> int64_t {
     const int32_t pidx = jj / Pi;
     return (int64_t)lds_pt[pidx - vp_first] * Pi + (jj - pidx * Pi);
@@ -450,6 +467,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
   // first 32 tokens); the swizzles leave row bit 5 alone, so token block
   // tb + 2 and the second half of a 64-token tile sit 32 rows further
   int koff[2][2], voff[2][4];
+  auto init_koff = [&]() {
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
     const int row = 16 * tb + j;
@@ -461,6 +479,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
       for (int par = 0; par < 2; ++par) koff[tb][par] = row * ROWB + 16 * ((4 * par + g) ^ swz<false>(row));
     }
   }
+  };
+  auto init_voff = [&]() {
   if (FP8) {
     const int s8 = (lane & 15) >> 1;
     const int vrow = s8 < 4 ? 4 * (lane >> 4) + s8 : 16 + 4 * (lane >> 4) + (s8 - 4);
@@ -475,6 +495,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
       for (int m = 0; m < 4; ++m) voff[h][m] = vrow * ROWB + 16 * ((2 * m) ^ y) + 8 * (lane & 1);
     }
   }
+  };
 
   float m_run = -INFINITY, l_run = 0.f;   // producer softmax state of row row0 + j
 
@@ -528,7 +549,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * PD, 0);
     } else {
       // fragment f = KU*tb + u: each accumulator takes its 18 MFMAs back to back
-      constexpr int NF = 2 * KU, PD = 8;
+      // (5 fragments ahead in 128 registers: 4 measured 1% slower, 6 spill)
+      constexpr int NF = 2 * KU, PD = LDW ? 5 : 8;
       bf16x8 kf[NF];
       auto ftb = [](int f) { return f / KU; };
       auto fu = [](int f) { return f % KU; };
@@ -659,29 +681,49 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_pc_kernel(DecodeParams
     }
   };
 
-  // stages 0 .. NSTG-2 in flight; stage 0 resident before the first tile
-  if (consumer) {
-    for (int s = 0; s < NSTG - 1 && s < n_st; ++s) issue(s, ALIGNED ? __builtin_amdgcn_readfirstlane(lds_pt[stage_pidx(s)]) : 0);
-    if (n_st > 0) wait_vmcnt_ahead<NI_MAX, NBIG, FP8, NSTG - 2>(lw, min(NSTG - 2, n_st - 1));
-  }
-  wg_barrier();
-  for (int i = 0; i <= n_st; ++i) {
-    const bool refill = i + NSTG - 1 < n_st;
-    int32_t pg_next = 0;
-    if (producer) {
-      if (i < n_st) produce(i);
-    } else if (consumer) {
-      // page id of the stage issued after this tile's barrier, read early
-      if (ALIGNED && refill) pg_next = lds_pt[stage_pidx(i + NSTG - 1)];
-      if (i >= 1) consume(i - 1);
-    }
-    if (i == n_st) break;
-    // stage i+1 must be resident for the next producer tile
-    if (consumer && i + 1 < n_st) wait_vmcnt_ahead<NI_MAX, NBIG, FP8, NSTG - 2>(lw, min(NSTG - 3, n_st - 2 - i));
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P^T and the rescale factors are in LDS
+  // one loop per role, so that each role's registers are live only in its own
+  // loop; every loop passes the workgroup barrier once before the first tile
+  // and once per tile (n_st times)
+  if (producer) {
+    init_koff();
     wg_barrier();
-    // the consumers are done with stage i-1: refill its slot
-    if (consumer && refill) issue(i + NSTG - 1, __builtin_amdgcn_readfirstlane(pg_next));
+    for (int i = 0; i < n_st; ++i) {
+      produce(i);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P^T and the rescale factors are in LDS
+      wg_barrier();
+    }
+  } else if (LDW && consumer) {
+    init_voff();
+    wg_barrier();
+    for (int i = 0; i < n_st; ++i) {
+      if (i >= 1) consume(i - 1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      wg_barrier();
+    }
+    if (n_st > 0) consume(n_st - 1);
+  } else {
+    if (consumer) init_voff();
+    if (loader) {
+      init_dma();
+      // stages 0 .. NSTG-2 in flight; stage 0 resident before the first tile
+      for (int s = 0; s < NSTG - 1 && s < n_st; ++s) issue(s, ALIGNED ? __builtin_amdgcn_readfirstlane(lds_pt[stage_pidx(s)]) : 0);
+      if (n_st > 0) wait_vmcnt_ahead<NI_MAX, NBIG, FP8, NSTG - 2>(lw, min(NSTG - 2, n_st - 1));
+    }
+    wg_barrier();
+    for (int i = 0; i <= n_st; ++i) {
+      const bool refill = i + NSTG - 1 < n_st;
+      int32_t pg_next = 0;
+      // page id of the stage issued after this tile's barrier, read early
+      if (loader && ALIGNED && refill) pg_next = lds_pt[stage_pidx(i + NSTG - 1)];
+      if (consumer && i >= 1) consume(i - 1);
+      if (i == n_st) break;
+      // stage i+1 must be resident for the next producer tile
+      if (loader && i + 1 < n_st) wait_vmcnt_ahead<NI_MAX, NBIG, FP8, NSTG - 2>(lw, min(NSTG - 3, n_st - 2 - i));
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      wg_barrier();
+      // the consumers are done with stage i-1: refill its slot
+      if (loader && refill) issue(i + NSTG - 1, __builtin_amdgcn_readfirstlane(pg_next));
+    }
   }
 
   // ---- finalise
@@ -1050,7 +1092,7 @@ __global__ void __launch_bounds__(256) split_combine_kernel(DecodeParams p) {
 
 template <int RGN, bool FP8>
 hipError_t launch_pc(const DecodeParams& prm, bool aligned, int64_t grid, hipStream_t stream) {
-  const dim3 g((unsigned)grid), b(kThreads);
+  const dim3 g((unsigned)grid), b(kPcThreads<RGN, FP8>);
   const bool nt = prm.n_row_blocks == 1;
   if (aligned && nt) hipLaunchKernelGGL((mla_decode_pc_kernel<RGN, FP8, true, true>), g, b, 0, stream, prm);
   else if (aligned) hipLaunchKernelGGL((mla_decode_pc_kernel<RGN, FP8, true, false>), g, b, 0, stream, prm);

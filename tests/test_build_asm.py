@@ -50,10 +50,22 @@ def test_decode_kernels_do_not_spill(asm):
         assert "scratch_" not in body, name
 
 
+def test_workgroup_sizes(asm):
+    # bf16 blocks of 64 rows (template arguments 4, false) run 16 waves with dedicated
+    # loading waves; every other instantiation 8 waves
+    # (the kernel metadata lists each kernel's workgroup size just before its name)
+    meta = {n: s for s, n in re.findall(r"\.max_flat_workgroup_size:\s+(\d+)\s+\.name:\s+(\S+)", asm)
+            if "mla_decode_pc_kernel" in n}
+    assert len(meta) == 24, sorted(meta)
+    for name, size in meta.items():
+        want = 1024 if "kernelILi4ELb0E" in name else 512
+        assert int(size) == want, (name, size)
+
+
 def test_no_compiler_vmcnt_waits_inside_decode_loop(asm):
     # every vmcnt wait of the decode kernels is one of the explicit ones: 0 (page table and
     # Q before the loop) or a whole number of stages of one wave's loads, at most two
-    # stages ahead.  A stage is 36 KB: 36 loads, 9 per consumer wave, plus one scale load
+    # stages ahead.  A stage is 36 KB: 36 loads, 9 per loading wave, plus one scale load
     # per wave for e4m3 (64 rows of 576 bytes).  A wait the compiler placed for Q inside
     # the loop would show up as a count such as 17, 16, ... 1.
     # Waits before the first direct-to-LDS load (reading seq_len for the work plan, Q
