@@ -911,26 +911,41 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   // short units fill the tail: a unit's rank counts the single units that
   // are longer, or as long with a lower index.
   __shared__ __attribute__((aligned(16))) int32_t s_key[1024];
+  __shared__ int32_t s_rank[1024];
   const bool sort_singles = !uniform && p.units <= 1024;
   int32_t single_rank = 0;
   if (sort_singles) {
     int32_t items = 0, len = 0;
     if (tid < p.units) plan_of(st0, items, len);
-    const int32_t key = (tid < p.units && items == 1) ? st0 : -1;
-    s_key[tid] = key;
+    s_key[tid] = (tid < p.units && items == 1) ? st0 : -1;
     __syncthreads();
-    if (key >= 0) {
-      // keys past the last unit are -1 and never count; four keys per read
-      const int32_t n4 = (p.units + 3) >> 2;
-      for (int32_t k4 = 0; k4 < n4; ++k4) {
-        const int4 o = *reinterpret_cast<const int4*>(&s_key[4 * k4]);
-        const int32_t k = 4 * k4;
-        single_rank += (o.x > key) || (o.x == key && k < tid);
-        single_rank += (o.y > key) || (o.y == key && k + 1 < tid);
-        single_rank += (o.z > key) || (o.z == key && k + 2 < tid);
-        single_rank += (o.w > key) || (o.w == key && k + 3 < tid);
+    // tpu consecutive threads (a power of two, within one wave) count for one
+    // unit, each over a slice of the keys; keys past the last unit are -1
+    // and never count; four keys per read
+    int tpu = 1;
+    while (tpu < 64 && tpu * 2 * p.units <= 1024) tpu *= 2;
+    const int u = tid / tpu, part = tid % tpu;
+    int32_t cnt = 0;
+    if (u < p.units) {
+      const int32_t key = s_key[u];
+      if (key >= 0) {
+        const int32_t n4 = (p.units + 3) >> 2;
+        const int32_t per = (n4 + tpu - 1) / tpu;
+        const int32_t k4e = min(n4, (part + 1) * per);
+        for (int32_t k4 = part * per; k4 < k4e; ++k4) {
+          const int4 o = *reinterpret_cast<const int4*>(&s_key[4 * k4]);
+          const int32_t k = 4 * k4;
+          cnt += (o.x > key) || (o.x == key && k < u);
+          cnt += (o.y > key) || (o.y == key && k + 1 < u);
+          cnt += (o.z > key) || (o.z == key && k + 2 < u);
+          cnt += (o.w > key) || (o.w == key && k + 3 < u);
+        }
       }
     }
+    for (int o = 1; o < tpu; o <<= 1) cnt += __shfl_xor(cnt, o);
+    if (u < p.units && part == 0) s_rank[u] = cnt;
+    __syncthreads();
+    if (tid < p.units) single_rank = s_rank[tid];
   }
   // item offsets: items of split units in the high 32 bits, single-item
   // units in the low 32 bits; a second scan numbers the split units

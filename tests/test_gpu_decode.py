@@ -44,6 +44,8 @@ CASES = [
     ("h32", W(index=54, H=32, c=2, P=64, fixed_len=500), None),
     ("h64", W(index=55, H=64, c=4, P=64, fixed_len=777), None),
     ("h128_two_blocks", W(index=56, H=128, c=2, P=64, fixed_len=300, B=2), None),
+    # 64-row bf16 blocks (16 waves) on pages a stage can straddle, with a split unit
+    ("h128_page16_splits", W(index=76, H=128, c=2, P=16, B=2), [20000, 333]),
     ("verify_h16_q4", W(index=57, H=16, q_len=4, c=4, P=64, fixed_len=203, B=2), None),
     ("verify_h128_q4", W(index=58, H=128, q_len=4, c=4, P=64, fixed_len=130), None),
     ("noncausal_q2", W(index=59, H=32, q_len=2, c=3, P=32, fixed_len=90, causal=False), None),
