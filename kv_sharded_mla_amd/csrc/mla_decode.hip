@@ -76,6 +76,7 @@ struct DecodeParams {
   int32_t* item_unit;    // [max_items]
   int32_t* item_jb;      // [max_items] first rank-local token of the item
   int32_t* item_je;      // [max_items] end of the item's tokens
+  int32_t* item_order;   // [max_items] dispatch position -> item
   int32_t* unit_first;   // [units] first item of the unit
   int32_t* unit_count;   // [units] items of the unit
   int32_t* split_units;  // [units] the units with several items
@@ -335,9 +336,14 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
 
   const WgUnit wu = wg_unit(blockIdx.x, p.n_row_blocks);
   const int rb = wu.rb;
-  const int64_t item = wu.unit;
-  // without a plan (every unit is one item) item i is unit i, whole
-  if (item >= (p.direct ? (int64_t)p.units : (int64_t)*p.n_items)) return;
+  // without a plan (every unit is one item) item i is unit i, whole; with
+  // one, workgroups take the items in the plan's dispatch order
+  const int64_t n_it = p.direct ? (int64_t)p.units : (int64_t)*p.n_items;
+  if (wu.unit >= n_it) return;
+  const int64_t item = p.direct ? wu.unit : (int64_t)p.item_order[wu.unit];
+  // the plan writes a permutation of the items; an entry outside it (a
+  // workspace not written by this call's plan) must not index past the plan
+  if ((uint64_t)item >= (uint64_t)n_it) return;
   const int32_t unit = p.direct ? (int32_t)item : p.item_unit[item];
   const int b = unit % p.batch;
   const int rl = unit / p.batch;
@@ -762,10 +768,12 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
 // work W over about items_target items per row block, which gives every CU
 // a few items and keeps the largest at about half of a CU's share; T is
 // clamped to [t_min, t_max] (t_max: an item's page ids fit the workgroup's
-// LDS table).  A unit of s stages gets ceil(s / T) items of equal length.
-// Units with several items are listed first, so the longest work is
-// dispatched first.  Every unit gets at least one item (an empty one for a
-// rank that sees no token), so its outputs are always written.
+// LDS table).  A unit of s stages gets ceil(s / T) items of equal length
+// (the last one possibly shorter).  The items' slots list the units with
+// several items first; a separate dispatch order hands the items to the
+// decode workgroups longest first when the lengths are ragged.  Every unit
+// gets at least one item (an empty one for a rank that sees no token), so
+// its outputs are always written.
 // Exclusive prefix sum over the 1024 threads of a workgroup (64-bit values):
 // wave scans with shuffles, then the 16 wave totals.  Returns the prefix and
 // sets total.
@@ -892,9 +900,9 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     len = (st + items - 1) / items;
     items = (st + len - 1) / len;
   };
-  // Units with several items are listed first, so the single-item units
-  // start after all of their items (a separate counting pass unless every
-  // unit fits one chunk of 1024).
+  // Slots: the items of units with several items first, then the
+  // single-item units (a separate counting pass unless every unit fits one
+  // chunk of 1024).
   int64_t multi_total = 0;
   if (p.units > 1024) {
     for (int32_t base = 0; base < p.units; base += 1024) {
@@ -906,46 +914,44 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
       multi_total += tot;
     }
   }
-  // With ragged lengths (and at most 1024 units) the single-item units are
-  // listed longest first, so that the longest work starts first and the
-  // short units fill the tail: a unit's rank counts the single units that
-  // are longer, or as long with a lower index.
-  __shared__ __attribute__((aligned(16))) int32_t s_key[1024];
-  __shared__ int32_t s_rank[1024];
-  const bool sort_singles = !uniform && p.units <= 1024;
-  int32_t single_rank = 0;
-  if (sort_singles) {
+  // Dispatch order.  With ragged lengths (and at most 1024 units) the units
+  // are dispatched longest item first, each unit's items one after another
+  // (ties by unit index), so the longest work starts first and the short
+  // items fill the tail; otherwise in the order of their slots (split units
+  // first).  A unit's first position sums the items of the units that come
+  // before it.  The slots (partials of split units) stay contiguous per unit
+  // for the combine.
+  __shared__ __attribute__((aligned(16))) int32_t s_ord[2][1024];  // key, items
+  __shared__ int32_t s_pos[1024];
+  const bool lpt = !uniform && p.units <= 1024;
+  if (lpt) {
     int32_t items = 0, len = 0;
     if (tid < p.units) plan_of(st0, items, len);
-    s_key[tid] = (tid < p.units && items == 1) ? st0 : -1;
+    // key: item length (clamped, it only orders the dispatch), then the unit
+    // index reversed, so that a larger key comes first; 0 past the last unit
+    s_ord[0][tid] = tid < p.units ? (min(len, (1 << 20) - 1) << 10 | (1023 - tid)) : 0;
+    s_ord[1][tid] = tid < p.units ? items : 0;
     __syncthreads();
     // tpu consecutive threads (a power of two, within one wave) count for one
-    // unit, each over a slice of the keys; keys past the last unit are -1
-    // and never count; four keys per read
+    // unit, each over a slice of whole groups of four units
     int tpu = 1;
     while (tpu < 64 && tpu * 2 * p.units <= 1024) tpu *= 2;
     const int u = tid / tpu, part = tid % tpu;
-    int32_t cnt = 0;
+    int32_t before = 0;
     if (u < p.units) {
-      const int32_t key = s_key[u];
-      if (key >= 0) {
-        const int32_t n4 = (p.units + 3) >> 2;
-        const int32_t per = (n4 + tpu - 1) / tpu;
-        const int32_t k4e = min(n4, (part + 1) * per);
-        for (int32_t k4 = part * per; k4 < k4e; ++k4) {
-          const int4 o = *reinterpret_cast<const int4*>(&s_key[4 * k4]);
-          const int32_t k = 4 * k4;
-          cnt += (o.x > key) || (o.x == key && k < u);
-          cnt += (o.y > key) || (o.y == key && k + 1 < u);
-          cnt += (o.z > key) || (o.z == key && k + 2 < u);
-          cnt += (o.w > key) || (o.w == key && k + 3 < u);
-        }
+      const int32_t key = s_ord[0][u];
+      const int32_t per = ((p.units + tpu - 1) / tpu + 3) & ~3;
+      const int32_t v0 = part * per, ve = min((p.units + 3) & ~3, v0 + per);
+      for (int32_t v = v0; v < ve; v += 4) {
+        const int4 k4 = *reinterpret_cast<const int4*>(&s_ord[0][v]);
+        const int4 n4 = *reinterpret_cast<const int4*>(&s_ord[1][v]);
+        before += (k4.x > key ? n4.x : 0) + (k4.y > key ? n4.y : 0) + (k4.z > key ? n4.z : 0) +
+                  (k4.w > key ? n4.w : 0);
       }
     }
-    for (int o = 1; o < tpu; o <<= 1) cnt += __shfl_xor(cnt, o);
-    if (u < p.units && part == 0) s_rank[u] = cnt;
+    for (int o = 1; o < tpu; o <<= 1) before += __shfl_xor(before, o);
+    if (u < p.units && part == 0) s_pos[u] = before;
     __syncthreads();
-    if (tid < p.units) single_rank = s_rank[tid];
   }
   // item offsets: items of split units in the high 32 bits, single-item
   // units in the low 32 bits; a second scan numbers the split units
@@ -964,14 +970,14 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     nsplit += carry_split;
     if (p.units <= 1024) multi_total = tot >> 32;
     if (u < p.units) {
-      int32_t first = items > 1 ? (int32_t)(off >> 32) : (int32_t)(multi_total + (off & 0xffffffffLL));
-      if (sort_singles && items == 1) first = (int32_t)multi_total + single_rank;
+      const int32_t first = items > 1 ? (int32_t)(off >> 32) : (int32_t)(multi_total + (off & 0xffffffffLL));
       p.unit_first[u] = first;
       p.unit_count[u] = items;
       for (int32_t k = 0; k < items; ++k) {
         p.item_unit[first + k] = u;
         p.item_jb[first + k] = k * len * p.stage_tok;
         p.item_je[first + k] = min((k + 1) * len, st) * p.stage_tok;
+        p.item_order[lpt ? s_pos[u] + k : first + k] = first + k;
       }
       if (items > 1) p.split_units[nsplit] = u;
     }
@@ -1196,7 +1202,7 @@ DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, in
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   pl.off_ws_lse = al((size_t)pl.max_items * pl.rows * kDv * sizeof(float));
   pl.off_ints = pl.off_ws_lse + al((size_t)pl.max_items * pl.rows * sizeof(float));
-  pl.workspace_bytes = pl.off_ints + al((size_t)(3 + 3 * pl.max_items + 3 * pl.units) * sizeof(int32_t));
+  pl.workspace_bytes = pl.off_ints + al((size_t)(3 + 4 * pl.max_items + 3 * pl.units) * sizeof(int32_t));
   return pl;
 }
 
@@ -1243,7 +1249,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   prm.item_unit = ints + 3;
   prm.item_jb = prm.item_unit + pl.max_items;
   prm.item_je = prm.item_jb + pl.max_items;
-  prm.unit_first = prm.item_je + pl.max_items;
+  prm.item_order = prm.item_je + pl.max_items;
+  prm.unit_first = prm.item_order + pl.max_items;
   prm.unit_count = prm.unit_first + pl.units;
   prm.split_units = prm.unit_count + pl.units;
   prm.dev_status = a.dev_status;
