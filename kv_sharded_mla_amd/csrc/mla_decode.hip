@@ -475,32 +475,32 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
   int koff[2][2], voff[2][4];
   auto init_koff = [&]() {
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int row = 16 * tb + j;
-    if (FP8) {
-      koff[tb][0] = row * ROWB + 16 * (g ^ swz<true>(row));
-      koff[tb][1] = koff[tb][0];
-    } else {
+    for (int tb = 0; tb < 2; ++tb) {
+      const int row = 16 * tb + j;
+      if (FP8) {
+        koff[tb][0] = row * ROWB + 16 * (g ^ swz<true>(row));
+        koff[tb][1] = koff[tb][0];
+      } else {
 #pragma unroll
-      for (int par = 0; par < 2; ++par) koff[tb][par] = row * ROWB + 16 * ((4 * par + g) ^ swz<false>(row));
+        for (int par = 0; par < 2; ++par) koff[tb][par] = row * ROWB + 16 * ((4 * par + g) ^ swz<false>(row));
+      }
     }
-  }
   };
   auto init_voff = [&]() {
-  if (FP8) {
-    const int s8 = (lane & 15) >> 1;
-    const int vrow = s8 < 4 ? 4 * (lane >> 4) + s8 : 16 + 4 * (lane >> 4) + (s8 - 4);
+    if (FP8) {
+      const int s8 = (lane & 15) >> 1;
+      const int vrow = s8 < 4 ? 4 * (lane >> 4) + s8 : 16 + 4 * (lane >> 4) + (s8 - 4);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) voff[0][m] = vrow * ROWB + 16 * (m ^ swz<true>(vrow)) + 8 * (lane & 1);
-  } else {
+      for (int m = 0; m < 4; ++m) voff[0][m] = vrow * ROWB + 16 * (m ^ swz<true>(vrow)) + 8 * (lane & 1);
+    } else {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int vrow = 16 * h + 4 * (lane >> 4) + ((lane >> 2) & 3);
-      const int y = ((lane & 3) >> 1) ^ swz<false>(vrow);
+      for (int h = 0; h < 2; ++h) {
+        const int vrow = 16 * h + 4 * (lane >> 4) + ((lane >> 2) & 3);
+        const int y = ((lane & 3) >> 1) ^ swz<false>(vrow);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) voff[h][m] = vrow * ROWB + 16 * ((2 * m) ^ y) + 8 * (lane & 1);
+        for (int m = 0; m < 4; ++m) voff[h][m] = vrow * ROWB + 16 * ((2 * m) ^ y) + 8 * (lane & 1);
+      }
     }
-  }
   };
 
   float m_run = -INFINITY, l_run = 0.f;   // producer softmax state of row row0 + j
