@@ -73,7 +73,9 @@ enum {
   DCP_DEV_OUT_OF_PAGES = 1,   /* allocator: free stack too short            */
   DCP_DEV_BAD_LENGTH = 2,     /* a length is negative, shrinks, or exceeds max_seq_len */
   DCP_DEV_TABLE_OVERFLOW = 3, /* a position needs a block-table column >= bt_stride */
-  DCP_DEV_BAD_PAGE = 4        /* a block-table entry is outside [0, num_pages) */
+  DCP_DEV_BAD_PAGE = 4,       /* a block-table entry is outside [0, num_pages) */
+  DCP_DEV_DECODE_STALLED = 5  /* decode: a wave stopped waiting for its partner
+                                 wave (never expected; the outputs are invalid) */
 };
 
 enum { DCP_KV_BF16 = 0, DCP_KV_FP8_E4M3 = 1 };
@@ -206,6 +208,10 @@ size_t mla_decode_workspace_size(const dcp_layout* layout, int32_t rank_count, i
  *   workspace    device scratch of at least mla_decode_workspace_size(...)
  *                bytes, 16-byte aligned; contents are scratch, and calls that
  *                share one workspace must not overlap in time
+ *
+ * Device status: DCP_DEV_BAD_LENGTH, DCP_DEV_TABLE_OVERFLOW and
+ * DCP_DEV_BAD_PAGE as above; DCP_DEV_DECODE_STALLED if a wave of the e4m3
+ * decode gave up its bounded wait for the wave it exchanges row maxima with.
  */
 int mla_decode_partial(const dcp_layout* layout, const void* pools, const float* pool_scales,
                        int32_t rank_begin, int32_t rank_count, const void* q, int32_t batch,

@@ -30,6 +30,7 @@ DEV_OUT_OF_PAGES = 1
 DEV_BAD_LENGTH = 2
 DEV_TABLE_OVERFLOW = 3
 DEV_BAD_PAGE = 4
+DEV_DECODE_STALLED = 5
 
 
 class DcpError(RuntimeError):

@@ -236,6 +236,7 @@ const char* dcp_status_string(int status) {
     case DCP_DEV_BAD_LENGTH: return "device: bad length";
     case DCP_DEV_TABLE_OVERFLOW: return "device: block table overflow";
     case DCP_DEV_BAD_PAGE: return "device: page id out of range";
+    case DCP_DEV_DECODE_STALLED: return "device: decode wave stopped waiting for its partner";
     default: return "unknown status";
   }
 }

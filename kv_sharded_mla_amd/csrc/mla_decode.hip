@@ -288,6 +288,12 @@ __device__ __forceinline__ int32_t visible_tokens(int32_t L, int32_t r, int32_t 
 //   e4m3 producer does not fit 128 registers with 64-token tiles, and 32-token
 //   e4m3 tiles with loader waves measured slower than 8 waves with 64-token
 //   tiles.
+// In the 8-wave e4m3 kernel for blocks of 64 rows the producers split each
+// 64-token tile instead: producer w scores 32 rows (two row blocks) over one
+// half of the tokens, so each K fragment it reads and converts feeds two
+// MFMAs (half the K reads and conversions of four 16-row producers; long
+// e4m3 workload 742/748 -> 706/701 us); the two producers of the same rows
+// exchange their tile's row maxima through LDS before the exponentials.
 template <int RGN, bool FP8>
 constexpr bool kLoaderWaves = RGN == 4 && !FP8;
 template <int RGN, bool FP8>
@@ -316,6 +322,11 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
   constexpr int NDBC = LDW ? 4 : 8;       // output blocks per consumer wave
   constexpr int SCW = STOK / NLW;         // e4m3 token scales loaded per loading wave
   constexpr int KU = FP8 ? 9 : 18;        // k units (k-steps, or e4m3 k-step pairs)
+  // e4m3 blocks of 64 rows: each producer scores 32 rows (two row blocks) over
+  // one 32-token half of every 64-token tile, so each K fragment it reads and
+  // converts feeds two MFMAs; the two producers of the same rows (waves w and
+  // w ^ 2) agree on the running maximum through LDS once per tile
+  constexpr bool TS = FP8 && RGN == 4 && !LDW;
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds_kv[NSTG * SBYTES];
   __shared__ __attribute__((aligned(16))) float lds_sc[FP8 ? NSTG * STOK : 4];
@@ -324,6 +335,9 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
   __shared__ float lds_alpha[2][RGN * 16];
   __shared__ __attribute__((aligned(16))) int lds_resc[2][4];  // read as one 16-byte vector
   __shared__ float lds_l[RGN * 16];
+  __shared__ float lds_lh[TS ? 2 : 1][TS ? RGN * 16 : 1];     // per-half row sums
+  __shared__ float lds_xmax[TS ? 2 : 1][TS ? 4 * 32 : 1];     // row maxima per producer
+  __shared__ int lds_xflag[4];                                  // tile a producer's maxima are for
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -332,6 +346,7 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
   const bool consumer = LDW ? (w >= 4 && w < 12) : w >= 4;
   const bool loader = LDW ? w >= 12 : w >= 4;  // with 8 waves the consumers load
   const int rbq = w & 3;                  // producer: its row block
+  const int pair = w & 1, half = w >> 1;  // token-split producer: rows 32*pair.., tokens 32*half..
   const int cq = LDW ? w - 4 : (w & 3);   // consumer: its column group
 
   const WgUnit wu = wg_unit(blockIdx.x, p.n_row_blocks);
@@ -361,6 +376,10 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
   const int32_t jlim = min(visible(row0 / p.heads), j_stop);
   // wave-uniform: every row of a 16-row block belongs to the same query index
   const int32_t jlim_s = __builtin_amdgcn_readfirstlane(jlim);
+  int32_t jlim_ts[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    jlim_ts[i] = __builtin_amdgcn_readfirstlane(min(visible((rb * MB + (2 * pair + i) * 16) / p.heads), j_stop));
   const int n_st = j_end > j_begin ? (j_end - j_begin + STOK - 1) / STOK : 0;
   // The row blocks of one item walk its tiles from different starting points
   // (block rb starts rb tiles ahead, wrapping around): the block
@@ -392,18 +411,24 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
     if (bad_page && p.dev_status) atomicMax(p.dev_status, DCP_DEV_BAD_PAGE);
   }
   if (tid < 8) lds_resc[tid >> 2][tid & 3] = -1;
+  if (tid < 4) lds_xflag[tid] = -1;
 
   // One register array serves both roles, which are fixed per wave: a
   // producer keeps its Q^T fragments (18 x 16 bytes) in R[0..17], a consumer
   // its O^T accumulators (NDBC column blocks x RGN row blocks).
-  constexpr int NR = NDBC * RGN > 18 ? NDBC * RGN : 18;
+  constexpr int NQ = TS ? 36 : 18;
+  constexpr int NR = NDBC * RGN > NQ ? NDBC * RGN : NQ;
   f32x4 R[NR];
   if (producer) {
-    const uint16_t* qrow = p.q + ((int64_t)b * p.rows + row0 + j) * kDqk;
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) {
-      const int col = FP8 ? 64 * (kk >> 1) + 16 * g + 8 * (kk & 1) : 32 * kk + 8 * g;
-      R[kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + col));
+    for (int i = 0; i < NQ / 18; ++i) {
+      const int qr = TS ? rb * MB + (2 * pair + i) * 16 : row0;
+      const uint16_t* qrow = p.q + ((int64_t)b * p.rows + qr + j) * kDqk;
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) {
+        const int col = FP8 ? 64 * (kk >> 1) + 16 * g + 8 * (kk & 1) : 32 * kk + 8 * g;
+        R[18 * i + kk] = __builtin_bit_cast(f32x4, *reinterpret_cast<const bf16x8*>(qrow + col));
+      }
     }
   } else {
 #pragma unroll
@@ -632,6 +657,105 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
     }
   };
 
+  // Token-split producer (e4m3 blocks of 64 rows): rows 32*pair..32*pair+31
+  // (row blocks 2*pair and 2*pair+1), tokens 32*half..32*half+31 of each
+  // 64-token tile.  Both producers of the same rows keep the same running
+  // maximum m2 (each sees the other's tile maximum before its exponentials)
+  // and their own partial sums l2 of their half, added up at the end.
+  float m2[2] = {-INFINITY, -INFINITY}, l2[2] = {0.f, 0.f};
+  auto produce_ts = [&](int t) {
+    const uint8_t* kv = lds_kv + (t % NSTG) * SBYTES;
+    const float* sc = lds_sc + (t % NSTG) * STOK + 32 * half;
+    const int32_t jt = j_begin + tile_of(t) * STOK + 32 * half;  // first token of this half
+    f32x4 sacc[2][2];  // [row block][16-token block of the half]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl) sacc[i][tl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int NF = 2 * KU, PD = 4;  // fragment f: token block f / KU, k unit f % KU
+    i32x4 kf[NF];
+    auto kload = [&](int f) {
+      return *reinterpret_cast<const i32x4*>(kv + koff[f / KU][0] + half * 32 * ROWB + 64 * (f % KU));
+    };
+#pragma unroll
+    for (int f = 0; f < PD; ++f) kf[f] = kload(f);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      if (f + PD < NF) kf[f + PD] = kload(f + PD);
+      const int tl = f / KU, u = f % KU;
+      const bf16x8 a0 = cvt_fp8x8(i32x2{kf[f][0], kf[f][1]});
+      const bf16x8 a1 = cvt_fp8x8(i32x2{kf[f][2], kf[f][3]});
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sacc[i][tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf(18 * i + 2 * u), sacc[i][tl], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sacc[i][tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf(18 * i + 2 * u + 1), sacc[i][tl], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
+#pragma unroll
+    for (int f = 0; f < NF - PD; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * PD, 0);
+    // scores in base 2 with the token scales, masked past the visible limit
+    float y[2][8], rmax[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[i][e] = sacc[i][e >> 2][e & 3] * sc[16 * (e >> 2) + 4 * g + (e & 3)] * p.scale_log2;
+      if (jt + 32 > jlim_ts[i]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[i][e] += (jt + 16 * (e >> 2) + 4 * g + (e & 3) >= jlim_ts[i]) ? -INFINITY : 0.f;
+      }
+      rmax[i] = wave_max_g(max3f(max3f(y[i][0], y[i][1], y[i][2]), max3f(y[i][3], y[i][4], y[i][5]), fmaxf(y[i][6], y[i][7])));
+    }
+    // exchange the row maxima of this half with the partner (same rows, the
+    // other half); the partner runs the same tiles, so the wait ends; it is
+    // bounded anyway, and a wave that gives up reports it
+    volatile float* xm = lds_xmax[t & 1];
+    volatile int* xf = lds_xflag;
+    if (g == 0) {
+      xm[w * 32 + j] = rmax[0];
+      xm[w * 32 + 16 + j] = rmax[1];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the maxima are in LDS before the flag
+    if (lane == 0) xf[w] = t;
+    const int partner = w ^ 2;
+    int spin = 0;
+    while (xf[partner] != t && spin < (1 << 20)) {
+      __builtin_amdgcn_s_sleep(1);
+      ++spin;
+    }
+    if (spin >= (1 << 20) && lane == 0 && p.dev_status) atomicMax(p.dev_status, DCP_DEV_DECODE_STALLED);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    bf16x8 pf[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float mt = fmaxf(rmax[i], xm[partner * 32 + 16 * i + j]);
+      float alpha = 1.f;
+      const bool resc = __any(mt > m2[i] + kTau);
+      if (mt > m2[i] + kTau) {
+        alpha = __builtin_amdgcn_exp2f(m2[i] - mt);
+        m2[i] = mt;
+      }
+      const float mref = m2[i] == -INFINITY ? 0.f : m2[i];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float pe = __builtin_amdgcn_exp2f(y[i][e] - mref);
+        psum += pe;
+        pe *= sc[16 * (e >> 2) + 4 * g + (e & 3)];
+        pf[i][e] = (__bf16)pe;
+      }
+      l2[i] = l2[i] * alpha + psum;
+      lds_p[t & 1][((2 * pair + i) * NH + half) * 64 + lane] = pf[i];
+      if (resc && half == 0) {
+        if (g == 0) lds_alpha[t & 1][(2 * pair + i) * 16 + j] = alpha;
+        if (lane == 0) lds_resc[t & 1][2 * pair + i] = t;
+      }
+    }
+  };
+
   auto consume = [&](int t) {
     const uint8_t* kv = lds_kv + (t % NSTG) * SBYTES;
     // P^T of the row blocks and the eight V^T fragments of 32-token half h
@@ -694,7 +818,8 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
     init_koff();
     wg_barrier();
     for (int i = 0; i < n_st; ++i) {
-      produce(i);
+      if constexpr (TS) produce_ts(i);
+      else produce(i);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P^T and the rescale factors are in LDS
       wg_barrier();
     }
@@ -734,7 +859,13 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
 
   // ---- finalise
   float* o_out = single ? p.o_part + (int64_t)unit * p.rows * kDv : p.ws_o + item * p.rows * kDv;
-  if (producer) {
+  if (producer && TS) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float lh = wave_sum_g(l2[i]);
+      if (g == 0) lds_lh[half][(2 * pair + i) * 16 + j] = lh;
+    }
+  } else if (producer) {
     const float l_tot = wave_sum_g(l_run);
     if (g == 0) {
       lds_l[rbq * 16 + j] = l_tot;
@@ -746,11 +877,23 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
     }
   }
   __syncthreads();
+  if (TS && producer && half == 0 && g == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = (2 * pair + i) * 16 + j;
+      const float l_tot = lds_lh[0][r] + lds_lh[1][r];
+      const float lse2 = l_tot > 0.f ? m2[i] + log2f(l_tot) : -INFINITY;
+      if (single)
+        p.lse_part[(int64_t)unit * p.rows + rb * MB + r] = p.out_base2 ? lse2 : lse2 * kLn2;
+      else
+        p.ws_lse[item * p.rows + rb * MB + r] = lse2;
+    }
+  }
   if (consumer) {
     const int64_t orow0 = rb * MB + j;
 #pragma unroll
     for (int q = 0; q < RGN; ++q) {
-      const float lq = lds_l[q * 16 + j];
+      const float lq = TS ? lds_lh[0][q * 16 + j] + lds_lh[1][q * 16 + j] : lds_l[q * 16 + j];
       const float inv = lq > 0.f ? 1.0f / lq : 0.f;
       float* optr = o_out + (orow0 + q * 16) * kDv;
 #pragma unroll

@@ -42,6 +42,7 @@ def test_status_strings(lib):
     assert dcp_status_string(0) == "ok"
     assert "out of pages" in dcp_status_string(1)
     assert "aligned" in dcp_status_string(-3)
+    assert "partner" in dcp_status_string(5)
     assert dcp_status_string(12345) == "unknown status"
 
 
