@@ -712,8 +712,10 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
     // exchange the row maxima of this half with the partner (same rows, the
     // other half); the partner runs the same tiles, so the wait ends; it is
     // bounded anyway, and a wave that gives up reports it
-    volatile float* xm = lds_xmax[t & 1];
-    volatile int* xf = lds_xflag;
+    // volatile LDS pointers (with the LDS address space, so that these stay
+    // ds_read / ds_write and are not turned into flat accesses)
+    volatile __attribute__((address_space(3))) float* xm = DCP_LDS(float, lds_xmax[t & 1]);
+    volatile __attribute__((address_space(3))) int* xf = DCP_LDS(int, lds_xflag);
     if (g == 0) {
       xm[w * 32 + j] = rmax[0];
       xm[w * 32 + 16 + j] = rmax[1];
@@ -722,7 +724,7 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
     if (lane == 0) xf[w] = t;
     const int partner = w ^ 2;
     int spin = 0;
-    while (xf[partner] != t && spin < (1 << 20)) {
+    while (__builtin_amdgcn_readfirstlane(xf[partner]) != t && spin < (1 << 20)) {
       __builtin_amdgcn_s_sleep(1);
       ++spin;
     }
