@@ -10,10 +10,11 @@
 // block table is the rank-local page table.
 //
 // Kernel shape.  A workgroup of 8 waves (16 for 64-row bf16 blocks) owns one
-// (rank, request, KV split, block of 16*RGN query rows).  KV is streamed through an LDS ring of 36 KB
-// stages (32 bf16 or 64 e4m3 tokens) filled by direct-to-LDS 16-byte loads
-// (global_load_lds_dwordx4); every latent row is read from HBM once per
-// workgroup and serves all of its query rows.  Per 32 tokens:
+// (rank, request, KV split, block of 16*RGN query rows).  KV is streamed
+// through an LDS ring of 36 KB stages (32 bf16 or 64 e4m3 tokens) filled by
+// direct-to-LDS 16-byte loads (global_load_lds_dwordx4); every latent row is
+// read from HBM once per workgroup and serves all of its query rows.  Per 32
+// tokens:
 //   S^T[32 tok x 16 rows] = K[32 x 576] . Q^T           (mfma 16x16x32 bf16, K from LDS,
 //                                                       Q^T held in registers)
 //   O^T[512 x 16 rows]   += V^T[512 x 32] . P^T         (V^T read from the same LDS rows
@@ -284,10 +285,9 @@ __device__ __forceinline__ int32_t visible_tokens(int32_t L, int32_t r, int32_t 
 //   registers each): waves 4-11 consume, wave 4+c owning columns
 //   [64c, 64c+64), and waves 12-15 only issue the loads.  Issuing a stage's
 //   loads holds the issuing wave for most of a tile; here no wave that
-//   computes is held (128-head workloads 5-7% faster than with 8 waves).  The
-//   e4m3 producer does not fit 128 registers with 64-token tiles, and 32-token
-//   e4m3 tiles with loader waves measured slower than 8 waves with 64-token
-//   tiles.
+//   computes is held (128-head workloads 5-7% faster than with 8 waves).
+//   Loading waves for e4m3 measured no faster: with 64-token tiles (the token
+//   scales read where used to fit 128 registers) or with 32-token tiles.
 // In the 8-wave e4m3 kernel for blocks of 64 rows the producers split each
 // 64-token tile instead: producer w scores 32 rows (two row blocks) over one
 // half of the tokens, so each K fragment it reads and converts feeds two
