@@ -10,7 +10,9 @@ q_len 8, 256 heads, 16 owner pools, 256-token pages, more than 1024 units
 (rank, request) in one call, and verification rows
 whose causal limit falls before position 0 (they see nothing: lse = -inf,
 o = 0, on every rank and after the merge); a zero and a negative softmax
-scale; e4m3 with base-2 LSE.  Each compares every request's merged output
+scale; e4m3 with base-2 LSE.  Sixty-four seeded random shapes draw heads,
+query rows, group size, page size, interleave, dtype, LSE base, causality
+and ragged lengths together.  Each compares every request's merged output
 and every rank's partial with the oracle at the stated tolerances.
 """
 import numpy as np
@@ -265,3 +267,31 @@ def test_workspace_contents_do_not_matter(fill):
             assert torch.equal(o, ref_o) and torch.equal(l, ref_l), (kv, fill, k)
         assert case.group.status() == 0
         check_case(case)
+
+
+def _random_case(seed):
+    """A seeded random decode shape: heads, query rows, group size, page size,
+    interleave, dtype, LSE base, causality and ragged lengths (some long enough
+    to split) drawn together, the oracle's work kept to a few seconds."""
+    rng = np.random.default_rng(1000 + seed)
+    H = int(rng.choice([16, 32, 64, 128]))
+    q_len = int(rng.choice([1, 1, 2, 4]))
+    c = int(rng.choice([1, 2, 3, 4, 8]))
+    P = int(rng.choice([1, 16, 32, 48, 64]))
+    il = int(rng.choice([d for d in (1, 1, 2, 4, 8, 16) if P % d == 0]))
+    kv = str(rng.choice(["bf16", "fp8"]))
+    B = int(rng.integers(1, 4))
+    budget = 3_000_000 // (H * q_len)          # sum of lengths the oracle does in seconds
+    lens = [int(x) for x in rng.integers(0, max(2, min(3000, budget // B)), B)]
+    if rng.random() < 0.5:                     # one request long enough for a split
+        lens[int(rng.integers(0, B))] = int(min(budget, rng.integers(6000, 12000)))
+    w = W(index=200 + seed, B=B, H=H, q_len=q_len, c=c, P=P, kv_dtype=kv, interleave=il,
+          lse_base=str(rng.choice(["e", "2"])), causal=bool(rng.random() < 0.8), fixed_len=None)
+    return w, lens
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_decode_random_shapes(seed):
+    w, lens = _random_case(seed)
+    log(f"random case {seed}: {w} lens {lens}")
+    check_case(Case(w, lens=lens))
