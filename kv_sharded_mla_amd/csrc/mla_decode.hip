@@ -1035,6 +1035,11 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   if (uniform) target = target > 1 ? target / 2 : 1;
   int64_t T = (W + target - 1) / target;
   T = T < p.t_min ? p.t_min : (T > p.t_max ? p.t_max : T);
+  // A unit of st stages gets ceil(st / T) items: equal ones when the units
+  // are about equally long; with ragged lengths items of T stages and a
+  // shorter last one (the last items then come in many lengths, and the
+  // longest-first dispatch below places them to fill the tail).  Item k
+  // covers stages [k len, min((k + 1) len, st)).
   auto plan_of = [&](int32_t st, int32_t& items, int32_t& len) {
     if (st == 0) {
       items = 1;
@@ -1042,6 +1047,10 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
       return;
     }
     items = (int32_t)((st + T - 1) / T);
+    if (!uniform) {
+      len = (int32_t)T;
+      return;
+    }
     len = (st + items - 1) / items;
     items = (st + len - 1) / len;
   };
@@ -1059,24 +1068,31 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
       multi_total += tot;
     }
   }
-  // Dispatch order.  With ragged lengths (and at most 1024 units) the units
-  // are dispatched longest item first, each unit's items one after another
-  // (ties by unit index), so the longest work starts first and the short
-  // items fill the tail; otherwise in the order of their slots (split units
-  // first).  A unit's first position sums the items of the units that come
-  // before it.  The slots (partials of split units) stay contiguous per unit
-  // for the combine.
-  __shared__ __attribute__((aligned(16))) int32_t s_ord[2][1024];  // key, items
-  __shared__ int32_t s_pos[1024];
+  // Dispatch order.  With ragged lengths (and at most 1024 units) the items
+  // are dispatched longest first, ties by unit and then by position in the
+  // unit, so the longest work starts first and the short items fill the
+  // tail; otherwise in the order of their slots (split units first).  No
+  // item is longer than T: the items of exactly T stages come first, in
+  // unit order (an exclusive scan of their counts), then each unit's shorter
+  // item (at most one per unit) at the count of the shorter items that are
+  // longer, or as long in an earlier unit.  The slots (partials of split
+  // units) stay contiguous per unit for the combine.
+  __shared__ __attribute__((aligned(16))) int32_t s_key[1024];
+  __shared__ int32_t s_pos[2][1024];  // first position of the T-stage items, of the shorter one
   const bool lpt = !uniform && p.units <= 1024;
   if (lpt) {
-    int32_t items = 0, len = 0;
-    if (tid < p.units) plan_of(st0, items, len);
-    // key: item length (clamped, it only orders the dispatch), then the unit
-    // index reversed, so that a larger key comes first; 0 past the last unit
-    s_ord[0][tid] = tid < p.units ? (min(len, (1 << 20) - 1) << 10 | (1023 - tid)) : 0;
-    s_ord[1][tid] = tid < p.units ? items : 0;
-    __syncthreads();
+    int32_t items = 0, len = 0, n_t = 0;
+    if (tid < p.units) {
+      plan_of(st0, items, len);
+      n_t = st0 > 0 ? st0 / len : 0;  // items of exactly T = len stages
+    }
+    const int32_t rest = st0 - n_t * len;  // the shorter item's stages (0: empty unit)
+    const bool has_rest = tid < p.units && n_t < items;
+    // key: the item's length (clamped, it only orders the dispatch), then
+    // the unit index reversed, so a larger key comes first; -1: no such item
+    s_key[tid] = has_rest ? (min(rest, (1 << 20) - 1) << 10 | (1023 - tid)) : -1;
+    int64_t n_t_total;
+    const int64_t t_before = block_excl_scan(n_t, wtot, n_t_total);
     // tpu consecutive threads (a power of two, within one wave) count for one
     // unit, each over a slice of whole groups of four units
     int tpu = 1;
@@ -1084,18 +1100,17 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     const int u = tid / tpu, part = tid % tpu;
     int32_t before = 0;
     if (u < p.units) {
-      const int32_t key = s_ord[0][u];
+      const int32_t key = s_key[u];
       const int32_t per = ((p.units + tpu - 1) / tpu + 3) & ~3;
       const int32_t v0 = part * per, ve = min((p.units + 3) & ~3, v0 + per);
       for (int32_t v = v0; v < ve; v += 4) {
-        const int4 k4 = *reinterpret_cast<const int4*>(&s_ord[0][v]);
-        const int4 n4 = *reinterpret_cast<const int4*>(&s_ord[1][v]);
-        before += (k4.x > key ? n4.x : 0) + (k4.y > key ? n4.y : 0) + (k4.z > key ? n4.z : 0) +
-                  (k4.w > key ? n4.w : 0);
+        const int4 k4 = *reinterpret_cast<const int4*>(&s_key[v]);
+        before += (k4.x > key) + (k4.y > key) + (k4.z > key) + (k4.w > key);
       }
     }
     for (int o = 1; o < tpu; o <<= 1) before += __shfl_xor(before, o);
-    if (u < p.units && part == 0) s_pos[u] = before;
+    if (tid < p.units) s_pos[0][tid] = (int32_t)t_before;
+    if (u < p.units && part == 0) s_pos[1][u] = (int32_t)n_t_total + before;
     __syncthreads();
   }
   // item offsets: items of split units in the high 32 bits, single-item
@@ -1122,7 +1137,12 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
         p.item_unit[first + k] = u;
         p.item_jb[first + k] = k * len * p.stage_tok;
         p.item_je[first + k] = min((k + 1) * len, st) * p.stage_tok;
-        p.item_order[lpt ? s_pos[u] + k : first + k] = first + k;
+        if (lpt) {
+          const int32_t n_t = st > 0 ? st / len : 0;
+          p.item_order[k < n_t ? s_pos[0][u] + k : s_pos[1][u]] = first + k;
+        } else {
+          p.item_order[first + k] = first + k;
+        }
       }
       if (items > 1) p.split_units[nsplit] = u;
     }
