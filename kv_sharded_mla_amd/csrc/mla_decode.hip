@@ -73,11 +73,11 @@ struct DecodeParams {
   int32_t max_items;
   int32_t items_target;  // work items per row block the plan aims for
   int32_t t_min, t_max;  // bounds of an item's length in stages
+  // [ceil8(max_items)][8] one record per dispatch position: item (its
+  // partial slot; -1 past the last item), unit, first and end rank-local
+  // token, the request's KV length, 1 when the unit is a single item, 0, 0
+  int32_t* drec;
   int32_t* n_items;      // [3]: work items, split units, most items of one unit
-  int32_t* item_unit;    // [max_items]
-  int32_t* item_jb;      // [max_items] first rank-local token of the item
-  int32_t* item_je;      // [max_items] end of the item's tokens
-  int32_t* item_order;   // [max_items] dispatch position -> item
   int32_t* unit_first;   // [units] first item of the unit
   int32_t* unit_count;   // [units] items of the unit
   int32_t* split_units;  // [units] the units with several items
@@ -351,26 +351,47 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
 
   const WgUnit wu = wg_unit(blockIdx.x, p.n_row_blocks);
   const int rb = wu.rb;
-  // without a plan (every unit is one item) item i is unit i, whole; with
-  // one, workgroups take the items in the plan's dispatch order
-  const int64_t n_it = p.direct ? (int64_t)p.units : (int64_t)*p.n_items;
-  if (wu.unit >= n_it) return;
-  const int64_t item = p.direct ? wu.unit : (int64_t)p.item_order[wu.unit];
-  // the plan writes a permutation of the items; an entry outside it (a
-  // workspace not written by this call's plan) must not index past the plan
-  if ((uint64_t)item >= (uint64_t)n_it) return;
-  const int32_t unit = p.direct ? (int32_t)item : p.item_unit[item];
+  // Without a plan (every unit is one item) item i is unit i, whole.  With
+  // one, the workgroups of dispatch position i read the plan's record i: a
+  // single load gives the item, its unit and token range, the request's
+  // length and whether the unit is split (each further dependent load would
+  // add a memory round trip before the first tile).  The plan writes every
+  // position the grid covers; a record outside its bounds (a workspace this
+  // call's plan did not write) ends the workgroup before it indexes anything.
+  // Item bounds and tile count are uniform: scalar registers.
+  int64_t item;
+  int32_t unit, L, j_begin, j_stop;
+  bool single;
+  if (p.direct) {
+    if (wu.unit >= p.units) return;
+    item = wu.unit;
+    unit = (int32_t)wu.unit;
+    L = request_len(p, unit % p.batch, tid == 0);
+    j_begin = 0;
+    j_stop = INT32_MAX;
+    single = true;
+  } else {
+    const int4* rec = reinterpret_cast<const int4*>(p.drec) + 2 * wu.unit;
+    const int4 r0 = rec[0], r1 = rec[1];
+    const int32_t it = __builtin_amdgcn_readfirstlane(r0.x);
+    unit = __builtin_amdgcn_readfirstlane(r0.y);
+    j_begin = __builtin_amdgcn_readfirstlane(r0.z);
+    j_stop = __builtin_amdgcn_readfirstlane(r0.w);
+    L = __builtin_amdgcn_readfirstlane(r1.x);
+    single = __builtin_amdgcn_readfirstlane(r1.y) != 0;
+    const int64_t vp = (int64_t)p.page * p.c;
+    if ((uint32_t)it >= (uint32_t)p.max_items || (uint32_t)unit >= (uint32_t)p.units || j_begin < 0 || L < 0 ||
+        (int64_t)L > p.max_seq_len || ((int64_t)L + vp - 1) / vp > p.bt_stride)
+      return;
+    item = it;
+  }
   const int b = unit % p.batch;
   const int rl = unit / p.batch;
   const int32_t ri = p.rank_begin + rl, Pi = p.page;
   const int row0 = rb * MB + rbq * 16;    // producer's first row
 
-  const int32_t L = request_len(p, b, tid == 0);
   // all rank-local token indices fit in int32 (seq_len is int32)
   auto visible = [&](int qi) -> int32_t { return visible_tokens(L, ri, p.c, p.interleave, p.q_len, qi, p.causal); };
-  // item bounds and tile count are uniform: scalar registers
-  const int32_t j_begin = p.direct ? 0 : __builtin_amdgcn_readfirstlane(p.item_jb[item]);
-  const int32_t j_stop = p.direct ? INT32_MAX : __builtin_amdgcn_readfirstlane(p.item_je[item]);
   const int32_t n_wg = visible((rb * MB + MB - 1) / p.heads);
   const int32_t j_end = __builtin_amdgcn_readfirstlane(min(n_wg, j_stop));
   const int32_t jlim = min(visible(row0 / p.heads), j_stop);
@@ -388,16 +409,16 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
   // tiles does not change the result beyond rounding.
   const int rot = n_st > 0 ? rb % n_st : 0;
   auto tile_of = [&](int s) { const int x = s + rot; return x < n_st ? x : x - n_st; };
-  // a unit with one item writes o_part / lse_part directly; the items of a
-  // split unit write partials (lse in base 2) for the combine, also when this
-  // row block sees none of the item's tokens (lse = -inf, o = 0)
-  const bool single = p.direct || p.unit_count[unit] == 1;
+  // a unit with one item writes o_part / lse_part directly (single); the
+  // items of a split unit write partials (lse in base 2) for the combine,
+  // also when this row block sees none of the item's tokens (lse = -inf, o = 0)
 
   const uint8_t* pool = p.pools + (int64_t)rl * p.pool_bytes;
   const float* spool = FP8 ? p.pool_scales + (int64_t)rl * p.cap : nullptr;
   const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
   const int32_t vp_first = j_begin / Pi;
   const int32_t n_tab = n_st > 0 ? (j_end - 1) / Pi - vp_first + 1 : 0;
+  if (n_tab > kMaxTab) return;  // the plan's item length keeps it within the table
   {
     bool bad_page = false;
     for (int t = tid; t < n_tab; t += NTHR) {
@@ -913,12 +934,14 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
 // work W over about items_target items per row block, which gives every CU
 // a few items and keeps the largest at about half of a CU's share; T is
 // clamped to [t_min, t_max] (t_max: an item's page ids fit the workgroup's
-// LDS table).  A unit of s stages gets ceil(s / T) items of equal length
-// (the last one possibly shorter).  The items' slots list the units with
-// several items first; a separate dispatch order hands the items to the
-// decode workgroups longest first when the lengths are ragged.  Every unit
-// gets at least one item (an empty one for a rank that sees no token), so
-// its outputs are always written.
+// LDS table).  A unit of s stages gets ceil(s / T) items: of equal length
+// when the units are about equally long, else of T stages and a shorter
+// last one.  The items' slots (where their partials go) list the units with
+// several items first; the decode workgroups take the items in a dispatch
+// order, longest first when the lengths are ragged, each position with a
+// record of everything the workgroup needs before its first load.  Every
+// unit gets at least one item (an empty one for a rank that sees no token),
+// so its outputs are always written.
 // Exclusive prefix sum over the 1024 threads of a workgroup (64-bit values):
 // wave scans with shuffles, then the 16 wave totals.  Returns the prefix and
 // sets total.
@@ -1008,18 +1031,24 @@ __device__ __forceinline__ void block_sum_max(int64_t v, int32_t m, int64_t* wto
 __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   __shared__ int64_t wtot[32];
   const int tid = threadIdx.x;
-  auto unit_stages = [&](int32_t u) -> int32_t {
+  // stages of unit u and its request's KV length (a length the decode cannot
+  // take is reported here and counts as 0; the decode reads it from the
+  // dispatch records)
+  auto unit_stages = [&](int32_t u, int32_t& L) -> int32_t {
     const int b = u % p.batch, rl = u / p.batch;
-    const int32_t L = request_len(p, b, false);
+    L = request_len(p, b, true);
     const int32_t n = visible_tokens(L, p.rank_begin + rl, p.c, p.interleave, p.q_len, p.q_len - 1, p.causal);
     return (n + p.stage_tok - 1) / p.stage_tok;
   };
-  // the first chunk's stage counts stay in a register (one read of seq_len)
-  const int32_t st0 = tid < p.units ? unit_stages(tid) : 0;
+  // the first chunk's stage counts and lengths stay in registers (one read
+  // of seq_len)
+  int32_t L0 = 0;
+  const int32_t st0 = tid < p.units ? unit_stages(tid, L0) : 0;
   int64_t w = st0;
   int32_t mx = st0;
   for (int32_t u = tid + 1024; u < p.units; u += 1024) {
-    const int32_t st = unit_stages(u);
+    int32_t Lu;
+    const int32_t st = unit_stages(u, Lu);
     w += st;
     mx = st > mx ? st : mx;
   }
@@ -1062,7 +1091,8 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     for (int32_t base = 0; base < p.units; base += 1024) {
       const int32_t u = base + tid;
       int32_t items = 0, len = 0;
-      if (u < p.units) plan_of(base == 0 ? st0 : unit_stages(u), items, len);
+      int32_t Lu;
+      if (u < p.units) plan_of(base == 0 ? st0 : unit_stages(u, Lu), items, len);
       int64_t tot;
       block_excl_scan(items > 1 ? items : 0, wtot, tot);
       multi_total += tot;
@@ -1118,9 +1148,9 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   int64_t carry = 0, carry_split = 0;
   for (int32_t base = 0; base < p.units; base += 1024) {
     const int32_t u = base + tid;
-    int32_t st = 0, items = 0, len = 0;
+    int32_t st = 0, items = 0, len = 0, L = L0;
     if (u < p.units) {
-      st = base == 0 ? st0 : unit_stages(u);
+      st = base == 0 ? st0 : unit_stages(u, L);
       plan_of(st, items, len);
     }
     int64_t tot, tot_split, off, nsplit;
@@ -1133,24 +1163,24 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
       const int32_t first = items > 1 ? (int32_t)(off >> 32) : (int32_t)(multi_total + (off & 0xffffffffLL));
       p.unit_first[u] = first;
       p.unit_count[u] = items;
+      const int32_t n_t = lpt && st > 0 ? st / len : 0;
       for (int32_t k = 0; k < items; ++k) {
-        p.item_unit[first + k] = u;
-        p.item_jb[first + k] = k * len * p.stage_tok;
-        p.item_je[first + k] = min((k + 1) * len, st) * p.stage_tok;
-        if (lpt) {
-          const int32_t n_t = st > 0 ? st / len : 0;
-          p.item_order[k < n_t ? s_pos[0][u] + k : s_pos[1][u]] = first + k;
-        } else {
-          p.item_order[first + k] = first + k;
-        }
+        const int32_t pos = !lpt ? first + k : (k < n_t ? s_pos[0][u] + k : s_pos[1][u]);
+        int4* rec = reinterpret_cast<int4*>(p.drec) + 2 * (int64_t)pos;
+        rec[0] = int4{first + k, u, k * len * p.stage_tok, min((k + 1) * len, st) * p.stage_tok};
+        rec[1] = int4{L, items == 1 ? 1 : 0, 0, 0};
       }
       if (items > 1) p.split_units[nsplit] = u;
     }
     carry += tot;
     carry_split += tot_split;
   }
+  // the positions past the last item that the decode grid covers
+  const int64_t n_total = multi_total + (carry & 0xffffffffLL);
+  for (int64_t pos = n_total + tid; pos < ((int64_t)p.max_items + 7) / 8 * 8; pos += 1024)
+    reinterpret_cast<int4*>(p.drec)[2 * pos] = int4{-1, 0, 0, 0};
   if (tid == 0) {
-    p.n_items[0] = (int32_t)(multi_total + (carry & 0xffffffffLL));
+    p.n_items[0] = (int32_t)n_total;
     p.n_items[1] = (int32_t)carry_split;
     int32_t items_max = 0, len = 0;
     plan_of(st_max, items_max, len);
@@ -1367,7 +1397,10 @@ DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, in
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   pl.off_ws_lse = al((size_t)pl.max_items * pl.rows * kDv * sizeof(float));
   pl.off_ints = pl.off_ws_lse + al((size_t)pl.max_items * pl.rows * sizeof(float));
-  pl.workspace_bytes = pl.off_ints + al((size_t)(3 + 4 * pl.max_items + 3 * pl.units) * sizeof(int32_t));
+  // dispatch records (8 ints for each position the decode grid covers), the
+  // item counts, then the per-unit lists
+  pl.workspace_bytes =
+      pl.off_ints + al((size_t)(8 * ((pl.max_items + 7) / 8 * 8) + 3 + 3 * pl.units) * sizeof(int32_t));
   return pl;
 }
 
@@ -1410,12 +1443,9 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   prm.ws_o = (float*)ws;
   prm.ws_lse = (float*)(ws + pl.off_ws_lse);
   int32_t* ints = (int32_t*)(ws + pl.off_ints);
-  prm.n_items = ints;
-  prm.item_unit = ints + 3;
-  prm.item_jb = prm.item_unit + pl.max_items;
-  prm.item_je = prm.item_jb + pl.max_items;
-  prm.item_order = prm.item_je + pl.max_items;
-  prm.unit_first = prm.item_order + pl.max_items;
+  prm.drec = ints;  // 256-byte aligned: records load as two 16-byte words
+  prm.n_items = ints + 8 * ((pl.max_items + 7) / 8 * 8);
+  prm.unit_first = prm.n_items + 3;
   prm.unit_count = prm.unit_first + pl.units;
   prm.split_units = prm.unit_count + pl.units;
   prm.dev_status = a.dev_status;
