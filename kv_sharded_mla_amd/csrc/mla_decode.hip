@@ -942,9 +942,10 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
 // record of everything the workgroup needs before its first load.  Every
 // unit gets at least one item (an empty one for a rank that sees no token),
 // so its outputs are always written.
-// Exclusive prefix sum over the 1024 threads of a workgroup (64-bit values):
-// wave scans with shuffles, then the 16 wave totals.  Returns the prefix and
+// Exclusive prefix sum over the NW waves of a workgroup (64-bit values):
+// wave scans with shuffles, then the wave totals.  Returns the prefix and
 // sets total.
+template <int NW>
 __device__ __forceinline__ int64_t block_excl_scan(int64_t v, int64_t* wtot, int64_t& total) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int64_t x = v;
@@ -957,7 +958,7 @@ __device__ __forceinline__ int64_t block_excl_scan(int64_t v, int64_t* wtot, int
   __syncthreads();
   int64_t before = 0;
   total = 0;
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const int64_t t = wtot[i];
     if (i < wv) before += t;
     total += t;
@@ -966,8 +967,9 @@ __device__ __forceinline__ int64_t block_excl_scan(int64_t v, int64_t* wtot, int
   return before + x - v;
 }
 
-// Two exclusive prefix sums over the 1024 threads at once (one pair of
-// barriers for both).
+// Two exclusive prefix sums over the NW waves at once (one pair of barriers
+// for both).
+template <int NW>
 __device__ __forceinline__ void block_excl_scan2(int64_t va, int64_t vb, int64_t* wtot, int64_t& pa, int64_t& pb,
                                                  int64_t& ta, int64_t& tb) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -989,7 +991,7 @@ __device__ __forceinline__ void block_excl_scan2(int64_t va, int64_t vb, int64_t
   ta = 0;
   tb = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const int64_t x = wtot[i], y = wtot[16 + i];
     if (i < wv) {
       ba += x;
@@ -1003,7 +1005,8 @@ __device__ __forceinline__ void block_excl_scan2(int64_t va, int64_t vb, int64_t
   pb = bb + b - vb;
 }
 
-// Sum and maximum over the 1024 threads of a workgroup (every thread gets both).
+// Sum and maximum over the NW waves of a workgroup (every thread gets both).
+template <int NW>
 __device__ __forceinline__ void block_sum_max(int64_t v, int32_t m, int64_t* wtot, int64_t& sum, int32_t& mx) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 #pragma unroll
@@ -1020,7 +1023,7 @@ __device__ __forceinline__ void block_sum_max(int64_t v, int32_t m, int64_t* wto
   sum = 0;
   mx = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NW; ++i) {
     sum += wtot[i];
     const int32_t y = (int32_t)wtot[16 + i];
     mx = y > mx ? y : mx;
@@ -1028,7 +1031,13 @@ __device__ __forceinline__ void block_sum_max(int64_t v, int32_t m, int64_t* wto
   __syncthreads();
 }
 
-__global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
+// NTHR threads (64, 256 or 1024): at least one per unit up to 1024 units, so
+// small batches plan in one or four waves instead of sixteen (the plan is a
+// chain of short dependent steps, and sixteen waves on four SIMDs take turns
+// at every one of them); the result does not depend on NTHR.
+template <int NTHR>
+__global__ void __launch_bounds__(NTHR) decode_plan_kernel(DecodeParams p) {
+  constexpr int NW = NTHR / 64;
   __shared__ int64_t wtot[32];
   const int tid = threadIdx.x;
   // stages of unit u and its request's KV length (a length the decode cannot
@@ -1046,7 +1055,7 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   const int32_t st0 = tid < p.units ? unit_stages(tid, L0) : 0;
   int64_t w = st0;
   int32_t mx = st0;
-  for (int32_t u = tid + 1024; u < p.units; u += 1024) {
+  for (int32_t u = tid + NTHR; u < p.units; u += NTHR) {
     int32_t Lu;
     const int32_t st = unit_stages(u, Lu);
     w += st;
@@ -1054,7 +1063,7 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   }
   int64_t W;
   int32_t st_max;
-  block_sum_max(w, mx, wtot, W, st_max);
+  block_sum_max<NW>(w, mx, wtot, W, st_max);
   // When the units are about equally long (the longest at most 1.25 x the
   // mean) there is no ragged tail to spread, and one item per CU and row
   // block beats two: each item pays a q load, a pipeline fill and, when its
@@ -1062,8 +1071,9 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   int64_t target = p.items_target;
   const bool uniform = (int64_t)st_max * p.units * 4 <= W * 5;
   if (uniform) target = target > 1 ? target / 2 : 1;
-  int64_t T = (W + target - 1) / target;
-  T = T < p.t_min ? p.t_min : (T > p.t_max ? p.t_max : T);
+  int64_t T64 = (W + target - 1) / target;
+  // within [t_min, t_max]: 32-bit from here on (item arithmetic stays in int32)
+  const int32_t T = (int32_t)(T64 < p.t_min ? p.t_min : (T64 > p.t_max ? p.t_max : T64));
   // A unit of st stages gets ceil(st / T) items: equal ones when the units
   // are about equally long; with ragged lengths items of T stages and a
   // shorter last one (the last items then come in many lengths, and the
@@ -1075,9 +1085,9 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
       len = 0;
       return;
     }
-    items = (int32_t)((st + T - 1) / T);
+    items = (st + T - 1) / T;  // st < 2^26 stages, T <= t_max: no overflow
     if (!uniform) {
-      len = (int32_t)T;
+      len = T;
       return;
     }
     len = (st + items - 1) / items;
@@ -1085,16 +1095,16 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   };
   // Slots: the items of units with several items first, then the
   // single-item units (a separate counting pass unless every unit fits one
-  // chunk of 1024).
+  // chunk of NTHR).
   int64_t multi_total = 0;
-  if (p.units > 1024) {
-    for (int32_t base = 0; base < p.units; base += 1024) {
+  if (p.units > NTHR) {
+    for (int32_t base = 0; base < p.units; base += NTHR) {
       const int32_t u = base + tid;
       int32_t items = 0, len = 0;
       int32_t Lu;
       if (u < p.units) plan_of(base == 0 ? st0 : unit_stages(u, Lu), items, len);
       int64_t tot;
-      block_excl_scan(items > 1 ? items : 0, wtot, tot);
+      block_excl_scan<NW>(items > 1 ? items : 0, wtot, tot);
       multi_total += tot;
     }
   }
@@ -1107,9 +1117,9 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   // item (at most one per unit) at the count of the shorter items that are
   // longer, or as long in an earlier unit.  The slots (partials of split
   // units) stay contiguous per unit for the combine.
-  __shared__ __attribute__((aligned(16))) int32_t s_key[1024];
-  __shared__ int32_t s_pos[2][1024];  // first position of the T-stage items, of the shorter one
-  const bool lpt = !uniform && p.units <= 1024;
+  __shared__ __attribute__((aligned(16))) int32_t s_key[NTHR];
+  __shared__ int32_t s_pos[2][NTHR];  // first position of the T-stage items, of the shorter one
+  const bool lpt = !uniform && p.units <= NTHR;  // NTHR >= units whenever units <= 1024
   if (lpt) {
     int32_t items = 0, len = 0, n_t = 0;
     if (tid < p.units) {
@@ -1122,21 +1132,25 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
     // the unit index reversed, so a larger key comes first; -1: no such item
     s_key[tid] = has_rest ? (min(rest, (1 << 20) - 1) << 10 | (1023 - tid)) : -1;
     int64_t n_t_total;
-    const int64_t t_before = block_excl_scan(n_t, wtot, n_t_total);
+    const int64_t t_before = block_excl_scan<NW>(n_t, wtot, n_t_total);
     // tpu consecutive threads (a power of two, within one wave) count for one
     // unit, each over a slice of whole groups of four units
     int tpu = 1;
-    while (tpu < 64 && tpu * 2 * p.units <= 1024) tpu *= 2;
+    while (tpu < 64 && tpu * 2 * p.units <= NTHR) tpu *= 2;
     const int u = tid / tpu, part = tid % tpu;
     int32_t before = 0;
     if (u < p.units) {
       const int32_t key = s_key[u];
       const int32_t per = ((p.units + tpu - 1) / tpu + 3) & ~3;
       const int32_t v0 = part * per, ve = min((p.units + 3) & ~3, v0 + per);
-      for (int32_t v = v0; v < ve; v += 4) {
+      auto count4 = [&](int32_t v) {
         const int4 k4 = *reinterpret_cast<const int4*>(&s_key[v]);
-        before += (k4.x > key) + (k4.y > key) + (k4.z > key) + (k4.w > key);
-      }
+        return (k4.x > key) + (k4.y > key) + (k4.z > key) + (k4.w > key);
+      };
+      // four LDS reads in flight per step: the loop is latency-bound
+      int32_t v = v0;
+      for (; v + 16 <= ve; v += 16) before += count4(v) + count4(v + 4) + count4(v + 8) + count4(v + 12);
+      for (; v < ve; v += 4) before += count4(v);
     }
     for (int o = 1; o < tpu; o <<= 1) before += __shfl_xor(before, o);
     if (tid < p.units) s_pos[0][tid] = (int32_t)t_before;
@@ -1146,7 +1160,7 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   // item offsets: items of split units in the high 32 bits, single-item
   // units in the low 32 bits; a second scan numbers the split units
   int64_t carry = 0, carry_split = 0;
-  for (int32_t base = 0; base < p.units; base += 1024) {
+  for (int32_t base = 0; base < p.units; base += NTHR) {
     const int32_t u = base + tid;
     int32_t st = 0, items = 0, len = 0, L = L0;
     if (u < p.units) {
@@ -1154,18 +1168,19 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
       plan_of(st, items, len);
     }
     int64_t tot, tot_split, off, nsplit;
-    block_excl_scan2(items > 1 ? ((int64_t)items << 32) : (int64_t)items, items > 1 ? 1 : 0, wtot, off, nsplit, tot,
-                     tot_split);
+    block_excl_scan2<NW>(items > 1 ? ((int64_t)items << 32) : (int64_t)items, items > 1 ? 1 : 0, wtot, off, nsplit,
+                         tot, tot_split);
     off += carry;
     nsplit += carry_split;
-    if (p.units <= 1024) multi_total = tot >> 32;
+    if (p.units <= NTHR) multi_total = tot >> 32;
     if (u < p.units) {
       const int32_t first = items > 1 ? (int32_t)(off >> 32) : (int32_t)(multi_total + (off & 0xffffffffLL));
       p.unit_first[u] = first;
       p.unit_count[u] = items;
       const int32_t n_t = lpt && st > 0 ? st / len : 0;
+      const int32_t pos_t = lpt ? s_pos[0][u] : first, pos_r = lpt ? s_pos[1][u] : first + n_t;
       for (int32_t k = 0; k < items; ++k) {
-        const int32_t pos = !lpt ? first + k : (k < n_t ? s_pos[0][u] + k : s_pos[1][u]);
+        const int32_t pos = k < n_t || !lpt ? pos_t + k : pos_r;
         int4* rec = reinterpret_cast<int4*>(p.drec) + 2 * (int64_t)pos;
         rec[0] = int4{first + k, u, k * len * p.stage_tok, min((k + 1) * len, st) * p.stage_tok};
         rec[1] = int4{L, items == 1 ? 1 : 0, 0, 0};
@@ -1177,7 +1192,7 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeParams p) {
   }
   // the positions past the last item that the decode grid covers
   const int64_t n_total = multi_total + (carry & 0xffffffffLL);
-  for (int64_t pos = n_total + tid; pos < ((int64_t)p.max_items + 7) / 8 * 8; pos += 1024)
+  for (int64_t pos = n_total + tid; pos < ((int64_t)p.max_items + 7) / 8 * 8; pos += NTHR)
     reinterpret_cast<int4*>(p.drec)[2 * pos] = int4{-1, 0, 0, 0};
   if (tid == 0) {
     p.n_items[0] = (int32_t)n_total;
@@ -1374,7 +1389,8 @@ DecodePlan plan_decode(int32_t c, int32_t interleave, int32_t page, bool fp8, in
   const int64_t cyc = (int64_t)interleave * c;
   const int64_t n_r_max = (max_seq_len + cyc - 1) / cyc * interleave;
   const int64_t stages_max = (n_r_max + stok - 1) / stok;
-  pl.t_max = (int32_t)std::max<int64_t>(1, (int64_t)(kMaxTab - 1) * page / stok);
+  // (capped at 2^27 stages, more than any unit holds: seq_len is int32)
+  pl.t_max = (int32_t)std::min<int64_t>(int64_t(1) << 27, std::max<int64_t>(1, (int64_t)(kMaxTab - 1) * page / stok));
   // the shortest item: kItemMinStages 32-token stages' worth of tokens
   pl.t_min = std::min<int32_t>(std::max<int32_t>(1, kItemMinStages * kStageTok / stok), pl.t_max);
   pl.items_target = std::max<int32_t>(1, kItemsPerCu * device_cu_count() / pl.n_row_blocks);
@@ -1454,7 +1470,12 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   prm.direct = pl.direct ? 1 : 0;
   hipError_t e = hipSuccess;
   if (!pl.direct) {
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, prm);
+    if (pl.units <= 64)
+      hipLaunchKernelGGL(decode_plan_kernel<64>, dim3(1), dim3(64), 0, stream, prm);
+    else if (pl.units <= 256)
+      hipLaunchKernelGGL(decode_plan_kernel<256>, dim3(1), dim3(256), 0, stream, prm);
+    else
+      hipLaunchKernelGGL(decode_plan_kernel<1024>, dim3(1), dim3(1024), 0, stream, prm);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
