@@ -237,7 +237,7 @@ __device__ __forceinline__ int32_t request_len(const DecodeParams& p, int b, boo
     if (report && p.dev_status) atomicMax(p.dev_status, DCP_DEV_BAD_LENGTH);
     return 0;
   }
-  if (((int64_t)L + vp - 1) / vp > p.bt_stride) {
+  if ((int64_t)L > (int64_t)p.bt_stride * vp) {  // ceil(L / vp) > bt_stride
     if (report && p.dev_status) atomicMax(p.dev_status, DCP_DEV_TABLE_OVERFLOW);
     return 0;
   }
@@ -379,9 +379,10 @@ __global__ void __launch_bounds__((kPcThreads<RGN, FP8>), 1) mla_decode_pc_kerne
     j_stop = __builtin_amdgcn_readfirstlane(r0.w);
     L = __builtin_amdgcn_readfirstlane(r1.x);
     single = __builtin_amdgcn_readfirstlane(r1.y) != 0;
+    // (ceil(L / vp) > bt_stride, without a 64-bit division)
     const int64_t vp = (int64_t)p.page * p.c;
     if ((uint32_t)it >= (uint32_t)p.max_items || (uint32_t)unit >= (uint32_t)p.units || j_begin < 0 || L < 0 ||
-        (int64_t)L > p.max_seq_len || ((int64_t)L + vp - 1) / vp > p.bt_stride)
+        (int64_t)L > p.max_seq_len || (int64_t)L > (int64_t)p.bt_stride * vp)
       return;
     item = it;
   }
