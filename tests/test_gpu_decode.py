@@ -7,7 +7,8 @@ base-2 LSE, pages that do not align with a stage, KV splits with their
 combine, the e4m3 format, interleave sizes I > 1 (runs of I positions
 per owner, including runs that leave whole ranks empty), and the limits:
 q_len 8, 256 heads, 16 owner pools, 256-token pages, more than 1024 units
-(rank, request) in one call, and verification rows
+(rank, request) in one call, unit counts on both sides of each size of the
+work plan's workgroup (64 / 65, 256 / 257), and verification rows
 whose causal limit falls before position 0 (they see nothing: lse = -inf,
 o = 0, on every rank and after the merge); a zero and a negative softmax
 scale; e4m3 with base-2 LSE.  Sixty-four seeded random shapes draw heads,
@@ -92,6 +93,13 @@ CASES = [
     # the single-item units)
     ("units_over_1024", W(index=74, H=16, c=4, P=16, B=260), _ragged(260, 7, {3: 12000, 130: 8000, 259: 12000})),
     ("units_1024_ragged", W(index=75, H=16, c=8, P=16, B=128), _ragged(128, 8, {0: 30000, 77: 9000})),
+    # the plan's workgroup is sized to the units (64, 256 or 1024 threads):
+    # ragged batches on both sides of each size, one of them with 64-row blocks
+    ("plan_64_units", W(index=101, H=16, c=4, P=16, B=16), _ragged(16, 9, {2: 6000})),
+    ("plan_65_units", W(index=102, H=16, c=5, P=16, B=13), _ragged(13, 10, {0: 5000})),
+    ("plan_65_units_h128", W(index=105, H=128, c=5, P=64, B=13), _ragged(13, 13, {4: 4000})),
+    ("plan_256_units", W(index=103, H=16, c=8, P=16, B=32), _ragged(32, 11, {5: 9000, 31: 4000})),
+    ("plan_257_units", W(index=104, H=16, c=1, P=16, B=257), _ragged(257, 12, {100: 7000})),
 ]
 
 
