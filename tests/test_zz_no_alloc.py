@@ -5,7 +5,9 @@ bit for bit (same work plan and kernels; only the scratch address differs), on
 two calls in a row with the second one smaller (the scratch keeps the first
 call's contents, which the second must not depend on), on the single-launch
 path and on the planned split path, and match the oracle; a call whose
-workspace would exceed the scratch is refused on the host.
+workspace would exceed the scratch is refused on the host; and one call
+captured in a HIP graph, replayed after seq_len changes, equals the eager
+call with the same lengths.
 """
 import numpy as np
 import pytest
@@ -78,3 +80,47 @@ def test_noalloc_refuses_a_call_beyond_the_scratch():
     assert e.value.status == -4
     torch.cuda.synchronize()
     assert not o.any() and not lse.any()      # nothing was enqueued
+
+
+def test_noalloc_call_in_a_graph_follows_new_lengths():
+    # the callers this entry point is for capture it in graphs: one captured call
+    # replayed after seq_len changes equals the eager call with the same lengths
+    import kv_sharded_mla_amd as K
+    w = W(index=125, H=128, c=4, B=4)
+    lens = [9000, 300, 5000, 17]
+    case = Case(w, lens=lens)
+    g = case.group
+    shape = (w.c, w.B, w.q_len, w.H, 512)
+    o_cap = torch.empty(shape, dtype=torch.float32, device="cuda")
+    l_cap = torch.empty(shape[:-1], dtype=torch.float32, device="cuda")
+
+    def call(o, lse):
+        K.mla_decode_partial_noalloc(g.layout, g.pools, g.pool_scales, 0, w.c, case.q, g.block_table, g.seq_len,
+                                     g.max_seq_len, w.sm_scale, K.LSE_BASE_E, w.causal, o, lse, g.dev_status)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(o_cap, l_cap)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(o_cap, l_cap)
+    torch.cuda.synchronize()
+    full = g.seq_len.clone()
+    for i, ls in enumerate([lens, [4000, 300, 100, 17], [9000, 0, 700, 17]]):
+        g.seq_len.copy_(torch.tensor(ls, dtype=torch.int32, device="cuda"))
+        ref_o = torch.full_like(o_cap, float("nan"))
+        ref_l = torch.full_like(l_cap, float("nan"))
+        call(ref_o, ref_l)
+        torch.cuda.synchronize()
+        o_cap.fill_(float("nan"))
+        l_cap.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(o_cap.cpu().numpy().view(np.uint32), ref_o.cpu().numpy().view(np.uint32)), (i, ls)
+        assert np.array_equal(l_cap.cpu().numpy().view(np.uint32), ref_l.cpu().numpy().view(np.uint32)), (i, ls)
+        log(f"no-alloc graph replay {i} lengths {ls}: bit-identical to the eager call")
+    g.seq_len.copy_(full)
+    assert g.status() == 0
