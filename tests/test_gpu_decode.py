@@ -15,8 +15,10 @@ scale; e4m3 with base-2 LSE.  Sixty-four seeded random shapes draw heads,
 query rows, group size, page size, interleave, dtype, LSE base, causality
 and ragged lengths together.  Each compares every request's merged output
 and every rank's partial with the oracle at the stated tolerances.  Repeated
-calls are bitwise stable, and two calls in flight on two streams at once
-give what they give alone.
+calls are bitwise stable, two calls in flight on two streams at once give
+what they give alone, and lengths, table sizes and page ids that only the
+device can see to be wrong are reported with their codes while the other
+requests stay right.
 """
 import numpy as np
 import pytest
@@ -332,3 +334,59 @@ def test_two_streams_at_once():
         assert np.array_equal(l.cpu().numpy().view(np.uint32), rl.view(np.uint32)), case.w
         assert case.group.status() == 0
     log("two streams at once: both calls bit-identical to their calls alone")
+
+
+def _decode_raw(case, seq_len, max_seq_len, block_table):
+    """One call with the given lengths, bound and table; returns outputs and the status code."""
+    import kv_sharded_mla_amd as K
+    w, g = case.w, case.group
+    o = torch.full((w.c, w.B, w.q_len, w.H, K.D_V), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((w.c, w.B, w.q_len, w.H), float("nan"), dtype=torch.float32, device="cuda")
+    n = K.mla_decode_workspace_size(g.layout, w.c, w.B, w.q_len, w.H, max_seq_len)
+    ws = torch.empty(max(n // 4, 4), dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.mla_decode_partial(g.layout, g.pools, g.pool_scales, 0, w.c, case.q, block_table, seq_len, max_seq_len,
+                         w.sm_scale, K.LSE_BASE_E, w.causal, o, lse, ws, status)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), lse.cpu().numpy(), int(status.item())
+
+
+@pytest.mark.parametrize("kind", ["bad_length", "table_overflow", "bad_page"])
+def test_decode_reports_bad_arguments_on_the_device(kind):
+    # Conditions only the device can see, forced from the host: a request longer
+    # than max_seq_len, one that needs more block-table columns than bt_stride,
+    # a block-table entry outside the pool.  The call reports the documented
+    # code; a request whose length it cannot take decodes as empty (lse = -inf,
+    # o = 0 on every rank), a bad page id reads page 0 instead (values
+    # unspecified, no access outside the pool), and the other requests are
+    # still right.
+    from parity import compare
+    import kv_sharded_mla_amd as K
+    w = W(index=128, H=16, c=4, P=16, B=3)
+    lens = [500, 300, 2000]
+    case = Case(w, lens=lens)
+    g = case.group
+    seq = g.seq_len.clone()
+    bt = g.block_table.clone()
+    max_len = g.max_seq_len
+    bad = 2
+    if kind == "bad_length":
+        max_len = 600                       # request 2 (2000) exceeds the bound
+        want = K.DEV_BAD_LENGTH
+    elif kind == "table_overflow":
+        bt = bt[:, :10].contiguous()        # 10 virtual pages of 64: 640 tokens; request 2 needs 32
+        want = K.DEV_TABLE_OVERFLOW
+    else:
+        bt[bad, 3] = g.num_pages + 5        # one page of request 2 outside the pool
+        want = K.DEV_BAD_PAGE
+    o, lse, st = _decode_raw(case, seq, max_len, bt)
+    assert st == want, (kind, st)
+    for b in range(w.B):
+        if b == bad and kind != "bad_page":
+            assert np.isneginf(lse[:, b]).all() and not o[:, b].any(), kind
+            continue
+        if b == bad:
+            continue
+        _, _, rop, rlp = case.oracle(b)
+        compare(f"{kind} b={b}", o[:, b], lse[:, b], rop, rlp, w.kv_dtype, partial=True)
+    log(f"{kind}: status {st}, the other requests right")
