@@ -209,6 +209,11 @@ size_t mla_decode_workspace_size(const dcp_layout* layout, int32_t rank_count, i
  *                bytes, 16-byte aligned; contents are scratch, and calls that
  *                share one workspace must not overlap in time
  *
+ * The call enqueues kernels only (no allocation, copy or memset), and the
+ * split of the work is decided on the device from seq_len at every call: a
+ * call captured in a HIP graph stays right when seq_len changes between
+ * replays, as long as every length stays within the captured max_seq_len.
+ *
  * Device status: DCP_DEV_BAD_LENGTH, DCP_DEV_TABLE_OVERFLOW and
  * DCP_DEV_BAD_PAGE as above; DCP_DEV_DECODE_STALLED if a wave of the e4m3
  * decode gave up its bounded wait for the wave it exchanges row maxima with.
