@@ -145,7 +145,7 @@ def roofline_of(w, flops, nbytes, t_ms):
                 frac=(tflops / MFMA_BF16_PEAK_TFLOPS) if mfma_bound else (gbps / HBM_PEAK_GBPS))
 
 
-def time_workload(w, steps, warmup, copies=2, share=True, decode_only=0, calib_copy_mib=0):
+def time_workload(w, steps, warmup, copies=2, share=True, decode_only=0, calib_copy_mib=0, graph=True):
     """Time `steps` layer-steps of workload w on resident pools; returns the measurements."""
     import numpy as np
     import torch
@@ -273,6 +273,44 @@ def time_workload(w, steps, warmup, copies=2, share=True, decode_only=0, calib_c
         r["t_share"] = sorted(a.elapsed_time(b) for a, b in ev)[len(ev) // 2]
     log(f"decode median {r['dec_med'] * 1e3:.1f} us, p90 {r['dec_p90'] * 1e3:.1f} us"
         + ("" if r["t_share"] is None else f"; one rank's share {r['t_share'] * 1e3:.1f} us"))
+    # The same layer-step captured in a HIP graph (one per pool copy) and replayed, as a serving
+    # loop that captures its decode step runs it: the host's per-call launch cost (ctypes and the
+    # binding's checks, four entry points per step) leaves the step.  Every replay does the whole
+    # step (page restore, allocation, scatter, decode with its device-side plan, merge); the
+    # outputs of the last replay must equal the eager step's bit for bit.
+    r["t_step_graph"] = None
+    if graph:
+        ref_o, ref_lse = o.clone(), lse.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0)  # warm the entry points on a side stream before capture, as torch asks
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for gi in range(len(groups)):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step(gi)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        r["t_step_graph"] = e0.elapsed_time(e1) / steps
+        assert all(g.status() == 0 for g in groups), [g.status() for g in groups]
+        assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), "graph replay output differs from eager"
+        assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), "graph replay lse differs from eager"
+        del graphs, ref_o, ref_lse
+        log(f"graph-replayed layer-step {r['t_step_graph'] * 1e3:.1f} us (outputs identical to the eager step)")
     for i in range(decode_only):
         g = groups[i % len(groups)]
         K.mla_decode_partial(g.layout, g.pools, g.pool_scales, 0, w.c, q, g.block_table, new_len, max_len,
@@ -298,7 +336,9 @@ def summary_of(w, r):
     roof = roofline_of(w, acct["flops"], acct["decode_bytes"], r["t_dec"])
     out = {"workload": w.name, "decode_us": round(r["t_dec"] * 1e3, 2),
            "decode_median_us": round(r["dec_med"] * 1e3, 2), "decode_p90_us": round(r["dec_p90"] * 1e3, 2),
-           "us_per_layer_step": round(r["wall_ms"] * 1e3, 2), "bound": roof["bound"], "frac": round(roof["frac"], 4),
+           "us_per_layer_step": round(r["wall_ms"] * 1e3, 2),
+           "us_per_layer_step_graph": None if r["t_step_graph"] is None else round(r["t_step_graph"] * 1e3, 2),
+           "bound": roof["bound"], "frac": round(roof["frac"], 4),
            "hbm_frac": round(roof["hbm_frac"], 4), "mfma_frac": round(roof["mfma_frac"], 4),
            "decode_gbps": round(roof["gbps"], 1), "decode_tflops": round(roof["tflops"], 2)}
     if r["t_share"] is not None:
@@ -328,6 +368,8 @@ def main():
                     help="skip timing one rank's share (profiling runs that should hold only group launches)")
     ap.add_argument("--op", choices=("step", "read", "relayout"), default="step",
                     help="what to time: the decode layer-step (default) or one of the layout copies")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replayed layer-step timing (profiling runs)")
     ap.add_argument("--decode-only", type=int, default=0,
                     help="after the timed steps, launch the decode entry point this many more times (profiling)")
     args = ap.parse_args()
@@ -351,7 +393,7 @@ def main():
     torch.cuda.set_device(0)
 
     r = time_workload(w, args.steps, args.warmup, args.copies, not args.no_share, args.decode_only,
-                      args.calib_copy_mib)
+                      args.calib_copy_mib, not args.no_graph)
     acct = r["acct"]
     lens, max_len = r["lens"], r["max_len"]
     ms_per_step = r["wall_ms"]
@@ -390,6 +432,7 @@ def main():
                    "interleave": w.interleave, "kv": w.kv_dtype, "context_tokens": int(lens.sum()), "max_len": max_len,
                    "lse_base": w.lse_base, "emulated_ranks_on_one_gpu": w.c},
         "us_per_layer_step": round(ms_per_step * 1e3, 2),
+        "us_per_layer_step_graph": None if r["t_step_graph"] is None else round(r["t_step_graph"] * 1e3, 2),
         "tflops": round(tflops, 2),
         "kernel_us": {"alloc+kv_write": round(r["t_write"] * 1e3, 2), "mla_decode_partial": round(r["t_dec"] * 1e3, 2),
                       "dcp_lse_merge": round(r["t_merge"] * 1e3, 2),
@@ -405,7 +448,8 @@ def main():
         out["workloads"] = {}
         for name in extras:
             we = configs.BY_NAME[name]
-            re_ = time_workload(we, args.extra_steps, min(args.warmup, 5), args.copies, not args.no_share)
+            re_ = time_workload(we, args.extra_steps, min(args.warmup, 5), args.copies, not args.no_share,
+                                graph=not args.no_graph)
             out["workloads"][name] = summary_of(we, re_)
     if not args.no_cpu_baseline:
         log(f"timing the oracle on the host for about {args.cpu_budget:.0f} s")

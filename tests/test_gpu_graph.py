@@ -75,3 +75,78 @@ def test_graph_replays_follow_new_lengths(kv, H):
                 compare(f"graph replay b={b}", got_o[:, b], got_l[:, b], rop, rlp, kv, partial=True)
     g.seq_len.copy_(full)
     assert g.status() == 0
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_layer_step_graph_matches_eager(kv):
+    # One whole layer-step (page-stack restore, allocation of the new tokens'
+    # pages, scatter of their rows, decode, merge) captured once and replayed,
+    # as a serving loop that captures its decode step runs it.  The last token
+    # of request 2 (position 256) opens a virtual page, so every step pops a
+    # page; each replay restores the stack top first and must pop the same one.
+    import kv_sharded_mla_amd as K
+    w = W(index=122 if kv == "bf16" else 123, kv_dtype=kv)
+    lens = np.array([3000, 700, 257, 64])
+    case = Case(w, lens=lens, keep_rows=True)
+    g = case.group
+    data, scale = case.rows
+    last = np.asarray(case.cu[1:]) - 1                      # each request's newest row
+    new_rows = torch.from_numpy(data.view(np.uint8).reshape(len(data), -1)[last]).to("cuda")
+    new_sc = torch.from_numpy(scale[last]).to("cuda") if scale is not None else None
+    old_len = torch.tensor(lens - 1, dtype=torch.int32, device="cuda")
+    new_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    cu_new = torch.arange(w.B + 1, dtype=torch.int32, device="cuda")
+    saved_top = g.free_top.clone()
+    ws = g.workspace_for(w.q_len, w.H)
+    o_part = torch.empty((w.c, w.B, w.q_len, w.H, 512), dtype=torch.float32, device="cuda")
+    lse_part = torch.empty(o_part.shape[:-1], dtype=torch.float32, device="cuda")
+    o = torch.empty((w.B, w.q_len, w.H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.q_len, w.H), dtype=torch.float32, device="cuda")
+
+    def step():
+        g.free_top.copy_(saved_top)
+        K.dcp_alloc_virtual(g.layout, g.free_stack, g.free_top, old_len, new_len, g.block_table, g.dev_status)
+        K.dcp_kv_write(g.layout, g.pools, g.pool_scales, g.block_table, new_len, cu_new, new_rows, new_sc, None,
+                       g.dev_status)
+        g.decode(case.q, w.sm_scale, K.LSE_BASE_E, w.causal, workspace=ws, out=(o_part, lse_part))
+        g.merge(o_part, lse_part, K.LSE_BASE_E, out=(o, lse))
+
+    def outputs():
+        torch.cuda.synchronize()
+        return [t.view(torch.int32 if t.dtype == torch.float32 else torch.int16).cpu().numpy()
+                for t in (o_part, lse_part, o, lse, g.block_table)]
+
+    step()
+    ref = outputs()
+    assert g.status() == 0, g.status()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        step()                                   # eager work between the replays
+        assert all(np.array_equal(a, b) for a, b in zip(outputs(), ref)), i
+        for t in (o_part, lse_part, lse):
+            t.fill_(float("nan"))
+        o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        got = outputs()
+        for name, a, b in zip(("o_part", "lse_part", "o", "lse", "block_table"), got, ref):
+            assert np.array_equal(a, b), (i, name)
+        log(f"{kv} layer-step replay {i}: bit-identical to the eager step")
+    assert g.status() == 0, g.status()
+    # and the step's outputs are the oracle's
+    o_f = o.float().cpu().numpy()
+    l_f = lse.cpu().numpy()
+    for b in range(w.B):
+        ro, rl, rop, rlp = case.oracle(b)
+        compare(f"layer-step graph b={b} merged", o_f[b], l_f[b], ro, rl, kv)
+        compare(f"layer-step graph b={b} partials", o_part[:, b].cpu().numpy(), lse_part[:, b].cpu().numpy(), rop, rlp,
+                kv, partial=True)
